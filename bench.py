@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the Sol-Attn block-sparse attention forward on one MI355X.
+
+One step = one forward over one batch of synthetic input: sol_route (block
+pooling, pooled scores, selection) followed by sol_attn_fwd (exact 951-token
+prefix sink plus the routed 64-token key blocks) at the pages' shape
+[1, 38247, 56, 128] bf16 with ~19% routed density.  Inputs are resident in
+HBM before the timed region.  Prints one JSON line on stdout; diagnostics go
+to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_page_sparse_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_sol_amd", "csrc", "attn.hip")
+
+
+def err(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(launch_bytes: float):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
+    or None when the kernel source changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    t = json.load(open(TRAFFIC_FILE))
+    if t.get("attn_src_sha256_16") != src_hash(ATTN_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q_bits, k_bits, v_bits, n_blocks: int, flop_eff: float):
+    """Time the oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+
+    import synth
+    from oracle import oracle as orc
+
+    heads = [0, 1]
+    qh, kh, vh = (synth.bf16_bits_to_f32(x[:, :, heads]) for x in (q_bits, k_bits, v_bits))
+    t0 = time.perf_counter()
+    r = orc.route(qh, kh, w.N, w.sink, w.tau)
+    t_route = time.perf_counter() - t0
+    g = r.geom
+    rng = np.random.default_rng(0)
+    blocks = [(0, int(rng.integers(len(heads))), int(rng.integers(g.NB))) for _ in range(n_blocks)]
+    flops = 0
+    for b, h, i in blocks:
+        keys = g.Ssink + sum(len(g.r_keys(j)) for j in np.nonzero(r.sel[b, h, i])[0])
+        flops += 4 * w.D * len(g.q_rows(i)) * keys
+    t0 = time.perf_counter()
+    orc.attention(qh, kh, vh, r.sel, g, blocks=blocks)
+    t_attn = time.perf_counter() - t0
+    # whole forward at these rates: routing per head x H, attention per query block x H*NB
+    t_forward = t_route / len(heads) * w.H + t_attn / n_blocks * w.H * g.NB
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    score_threads = min(8, os.cpu_count() or 1)
+    return {
+        "value": flop_eff / t_forward / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(max(blas_threads, score_threads)),
+        "kind": "oracle",
+        "sample": (f"oracle routing (float32 pool/score/select) of heads {heads} in "
+                   f"{t_route:.2f} s and float64 attention of {n_blocks} seeded query blocks "
+                   f"({flops / 1e9:.1f} GFLOP) in {t_attn:.2f} s; rate for the whole forward = "
+                   f"effective FLOP / (route time per head x {w.H} + attention time per block x "
+                   f"{w.H * g.NB}) = {t_forward:.0f} s per forward; host cpu_count "
+                   f"{os.cpu_count()}"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="page", choices=["page", "page_dense", "mid"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=48)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        err(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+            f"WORLD_SIZE {world}); the path shards by head across GPUs but no multi-GPU "
+            "run is built here")
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_sol_amd as sol
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dense = w.dense
+    t0 = time.perf_counter()
+    q_bits, k_bits, v_bits = synth.make_qkv(w)
+    err(f"generated {w.name} inputs in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+
+    def to_dev(b):
+        return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    o = torch.empty_like(q)
+    ws = torch.empty(max(sol.route_workspace_bytes(q), 256), dtype=torch.uint8, device=dev)
+    outs = sol.route_outputs(q)
+    idx, cnt, totals = outs
+
+    def step():
+        if dense:
+            sol.attn_dense(q, k, v, out=o)
+        else:
+            sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs)
+            sol.attn(q, k, v, idx, cnt, w.sink, out=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel events on the stream the kernels run on (torch's current stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        ev[s][0].record()
+        if not dense:
+            sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs)
+        ev[s][1].record()
+        if dense:
+            sol.attn_dense(q, k, v, out=o)
+        else:
+            sol.attn(q, k, v, idx, cnt, w.sink, out=o)
+        ev[s][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / args.steps
+    route_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    t_route = float(np.mean(route_ms)) if not dense else 0.0
+    t_attn = float(np.mean(attn_ms))
+
+    B, N, H, D = w.B, w.N, w.H, w.D
+    NB = sol.num_blocks(N)
+    Ssink = min(w.sink, N)
+    if dense:
+        pairs = B * H * N * N
+        routed = B * H * NB * NB
+        ncand = NB
+    else:
+        tot = totals.cpu().numpy()
+        routed, pairs = int(tot[0]), int(tot[1])
+        ncand = NB - (NB if w.sink >= N else w.sink // 64)
+    flop_eff = 4.0 * D * pairs
+    rho_route = routed / (B * H * NB * ncand)
+    rho_pair = pairs / (B * H * N * N)
+    tflops = flop_eff / (ms_step * 1e-3) / 1e12
+    attn_tflops = flop_eff / (t_attn * 1e-3) / 1e12
+    route_bytes = (B * N * H * D * 2 + B * max(N - Ssink, 0) * H * D * 2
+                   + 2 * routed + 4 * B * H * NB + 16) if not dense else 0
+    route_gbs = route_bytes / (t_route * 1e-3) / 1e9 if not dense else None
+    err(f"{w.name}: {ms_step:.3f} ms/forward (route {t_route:.3f} ms, attention {t_attn:.3f} ms), "
+        f"effective {tflops:.1f} TFLOP/s, attention {attn_tflops:.1f} TFLOP/s "
+        f"({attn_tflops / PEAK_BF16_TFLOPS:.1%} of bf16 peak), routing "
+        f"{(route_gbs or 0):.0f} GB/s; route density {rho_route:.4%}, pair density {rho_pair:.4%}; "
+        f"wall {wall:.2f} s for {args.steps} steps")
+
+    traffic = measured_traffic(flop_eff)
+    rec = {
+        "metric": "ms/forward + effective TFLOP/s (MFMA % peak) at [1,38247,56,128], ~19% density",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name}: one Sol-Attn forward (routing + sink/routed attention) on "
+                         f"[{B},{N},{H},{D}] bf16, sink {w.sink}, 64-token blocks, tau {w.tau}"
+                         if not dense else
+                         f"{w.name}: dense attention (routing disabled) on [{B},{N},{H},{D}] bf16"),
+            "B": B, "N": N, "H": H, "D": D, "sink": w.sink, "tau": w.tau,
+            "route_density": round(rho_route, 6), "pair_density": round(rho_pair, 6),
+            "routed_block_pairs": routed, "attended_pairs": pairs,
+            "route_ms": round(t_route, 4), "attn_ms": round(t_attn, 4),
+            "route_gbs": round(route_gbs, 1) if route_gbs else None,
+            "route_hbm_frac": round(route_gbs / PEAK_HBM_GBS, 4) if route_gbs else None,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        rec["cpu_baseline"] = cpu_baseline(w, q_bits, k_bits, v_bits, args.cpu_blocks, flop_eff)
+        err(f"cpu baseline took {time.perf_counter() - t0:.1f} s")
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,292 @@
+// Online block routing for Sol-Attn on gfx950: block-mean pooling of Q and K,
+// pooled scores in a fixed float32 order, and per-query-block selection under
+// threshold tau with the diagonal forced, written as compact ascending lists.
+//
+// Routing from compressed queries and keys under tau with a "diagonal
+// threshold" is named on the clawpit.io article (paragraph on the Sol-Attn
+// settings) and the nvlabs Sol-Engine H3 page (policy paragraph); the pages
+// give no formula.  The rule implemented (gap to the row maximum, diagonal
+// always kept) and its exact float32 order are stated in include/sol.h.
+//
+// Two kernels:
+//   pool_kernel          HBM-bound scan of Q and K (each element read once);
+//                        one lane owns 8 channels of one head and adds the
+//                        block's rows in ascending order.
+//   score_select_kernel  one lane owns one candidate key block and keeps its
+//                        pooled key (D floats) in registers; pooled query rows
+//                        are wave-uniform and come through the scalar cache;
+//                        each score is an FMA chain over d ascending.
+#include "sol_internal.h"
+
+namespace sol {
+
+namespace {
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ void add8(float (&acc)[8], const uint4& w) {
+    acc[0] += bf_lo(w.x); acc[1] += bf_hi(w.x);
+    acc[2] += bf_lo(w.y); acc[3] += bf_hi(w.y);
+    acc[4] += bf_lo(w.z); acc[5] += bf_hi(w.z);
+    acc[6] += bf_lo(w.w); acc[7] += bf_hi(w.w);
+}
+
+// grid: x = token block, y = lane groups of 256 over H * D / 8, z = batch * 2 + (0: Q, 1: K)
+// qbar: [B, H, NB, D] float32; kbar: [B, H, D / 8, NB, 8] float32 (8-channel
+// chunks, so a lane owning one key block reads its chunk contiguously).
+__global__ __launch_bounds__(256) void pool_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom g,
+    float* __restrict__ qbar, float* __restrict__ kbar, int64_t* __restrict__ totals)
+{
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+        totals[0] = 0;
+        totals[1] = 0;
+    }
+    const int blk = blockIdx.x;
+    const int b = blockIdx.z >> 1;
+    const int is_k = blockIdx.z & 1;
+    const int chunks = g.D >> 3;
+    const int lane_id = blockIdx.y * 256 + threadIdx.x;
+    if (lane_id >= g.H * chunks) return;
+    const int h = lane_id / chunks, c = lane_id - h * chunks;
+    int r0 = blk * kBlock;
+    const int r1 = min(r0 + kBlock, g.N);
+    if (is_k) {
+        if (blk < g.j0) return;
+        r0 = max(r0, g.S);
+    }
+    const uint16_t* src = (is_k ? k : q) + (int64_t)b * g.sb + (int64_t)h * g.sh + c * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int t = r0;
+    // rows strictly in ascending order; loads are issued 16 ahead
+    for (; t + 16 <= r1; t += 16) {
+        uint4 w[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            w[u] = *(const uint4*)(src + (int64_t)(t + u) * g.sn);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) add8(acc, w[u]);
+    }
+    for (; t < r1; ++t) add8(acc, *(const uint4*)(src + (int64_t)t * g.sn));
+    const float rows = (float)(r1 - r0);
+    const int64_t bh = (int64_t)b * g.H + h;
+    if (!is_k) {
+        float4* dst = (float4*)(qbar + (bh * g.NB + blk) * g.D + c * 8);
+        dst[0] = make_float4(acc[0] / rows, acc[1] / rows, acc[2] / rows, acc[3] / rows);
+        dst[1] = make_float4(acc[4] / rows, acc[5] / rows, acc[6] / rows, acc[7] / rows);
+    } else {
+        float4* dst = (float4*)(kbar + ((bh * chunks + c) * g.NB + blk) * 8);
+        dst[0] = make_float4(acc[0] / rows, acc[1] / rows, acc[2] / rows, acc[3] / rows);
+        dst[1] = make_float4(acc[4] / rows, acc[5] / rows, acc[6] / rows, acc[7] / rows);
+    }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+__device__ __forceinline__ long long wave_sum(long long v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+constexpr int kMaxWaves = 8;
+
+// grid: x = query-block tiles of TI (XCD-remapped together with y), y = B * H
+// block: 64 * W threads; lane slot s = jj * 64 W + tid owns candidate j = j0 + s.
+template <int D, int JPL, int TI>
+__global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, Geom g, float scale,
+    float tau, int tiles_per_bh, int16_t* __restrict__ idx, int32_t* __restrict__ cnt,
+    int64_t* __restrict__ totals)
+{
+    const int work = xcd_remap(blockIdx.x, gridDim.x, tiles_per_bh * g.B * g.H);
+    if (work < 0) return;
+    const int bh = work / tiles_per_bh;
+    const int i0 = (work - bh * tiles_per_bh) * TI;
+    const int ni = min(TI, g.NB - i0);
+    const int W = blockDim.x >> 6;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int slots = 64 * W;
+
+    __shared__ float red[TI][kMaxWaves];
+    __shared__ int wcount[TI][JPL * kMaxWaves];
+    __shared__ int woffset[TI][JPL * kMaxWaves];
+
+    const float* qb = qbar + (int64_t)bh * g.NB * D;
+    const float* kb = kbar + (int64_t)bh * (D / 8) * g.NB * 8;
+
+    float sc[JPL][TI];
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj) {
+        const int s = jj * slots + tid;
+        const bool valid = s < g.ncand;
+        const int j = g.j0 + (valid ? s : 0);
+        float kv[D];
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            const float4* p = (const float4*)(kb + ((int64_t)c * g.NB + j) * 8);
+            const float4 a = p[0], b = p[1];
+            kv[8 * c + 0] = a.x; kv[8 * c + 1] = a.y; kv[8 * c + 2] = a.z; kv[8 * c + 3] = a.w;
+            kv[8 * c + 4] = b.x; kv[8 * c + 5] = b.y; kv[8 * c + 6] = b.z; kv[8 * c + 7] = b.w;
+        }
+#pragma unroll
+        for (int ii = 0; ii < TI; ++ii) {
+            float acc = 0.f;
+            if (ii < ni) {
+                const float* qr = qb + (int64_t)(i0 + ii) * D;
+#pragma unroll
+                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qr[d], kv[d], acc);
+            }
+            const float v = acc * scale;
+            sc[jj][ii] = valid ? v : -INFINITY;
+        }
+    }
+
+    // row maxima over all candidates of the workgroup
+#pragma unroll
+    for (int ii = 0; ii < TI; ++ii) {
+        float m = sc[0][ii];
+#pragma unroll
+        for (int jj = 1; jj < JPL; ++jj) m = fmaxf(m, sc[jj][ii]);
+        m = wave_max(m);
+        if (lane == 0) red[ii][wave] = m;
+    }
+    __syncthreads();
+    float thr[TI];
+#pragma unroll
+    for (int ii = 0; ii < TI; ++ii) {
+        float m = red[ii][0];
+        for (int w = 1; w < W; ++w) m = fmaxf(m, red[ii][w]);
+        thr[ii] = m - tau;
+    }
+
+    // selection: count per (query block, slot group, wave)
+    long long keys_local = 0;
+#pragma unroll
+    for (int ii = 0; ii < TI; ++ii) {
+        const int i = i0 + ii;
+#pragma unroll
+        for (int jj = 0; jj < JPL; ++jj) {
+            const int s = jj * slots + tid;
+            const int j = g.j0 + s;
+            const bool sel = (ii < ni) && (s < g.ncand) && (sc[jj][ii] >= thr[ii] || j == i);
+            const uint64_t bal = __ballot(sel);
+            if (lane == 0) wcount[ii][jj * W + wave] = __popcll(bal);
+            if (sel) {
+                const int rows = min(kBlock, g.N - kBlock * i);
+                const int keys = min(kBlock * j + kBlock, g.N) - max(kBlock * j, g.S);
+                keys_local += (long long)rows * keys;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < ni) {
+        int run = 0;
+        for (int e = 0; e < JPL * W; ++e) {
+            const int jj = e / W, w = e - jj * W;
+            woffset[tid][jj * W + w] = run;
+            run += wcount[tid][jj * W + w];
+        }
+        cnt[(int64_t)bh * g.NB + i0 + tid] = run;
+        const int rows = min(kBlock, g.N - kBlock * (i0 + tid));
+        atomicAdd((unsigned long long*)&totals[0], (unsigned long long)run);
+        atomicAdd((unsigned long long*)&totals[1], (unsigned long long)rows * g.Ssink);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ii = 0; ii < TI; ++ii) {
+        const int i = i0 + ii;
+        int16_t* row = idx + ((int64_t)bh * g.NB + (ii < ni ? i : 0)) * g.NB;
+#pragma unroll
+        for (int jj = 0; jj < JPL; ++jj) {
+            const int s = jj * slots + tid;
+            const int j = g.j0 + s;
+            const bool sel = (ii < ni) && (s < g.ncand) && (sc[jj][ii] >= thr[ii] || j == i);
+            const uint64_t bal = __ballot(sel);
+            if (sel) row[woffset[ii][jj * W + wave] + lanes_below(bal)] = (int16_t)j;
+        }
+    }
+    keys_local = wave_sum(keys_local);
+    if (lane == 0 && keys_local != 0)
+        atomicAdd((unsigned long long*)&totals[1], (unsigned long long)keys_local);
+}
+
+// S >= N: no candidates, every list is empty, only sink pairs are attended.
+__global__ __launch_bounds__(256) void empty_route_kernel(int32_t* __restrict__ cnt, int n,
+                                                          int64_t* __restrict__ totals,
+                                                          long long sink_pairs)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) cnt[i] = 0;
+    if (i == 0) {
+        totals[0] = 0;
+        totals[1] = sink_pairs;
+    }
+}
+
+template <int D>
+hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, float scale,
+                         float tau, int16_t* idx, int32_t* cnt, int64_t* totals,
+                         hipStream_t stream)
+{
+    const int jpl = (g.ncand + 64 * kMaxWaves - 1) / (64 * kMaxWaves);
+    const int W = (g.ncand + 64 * jpl - 1) / (64 * jpl);
+#define SOL_SELECT_CASE(J, T)                                                               \
+    do {                                                                                    \
+        const int tiles = (g.NB + (T) - 1) / (T);                                           \
+        const int total = tiles * g.B * g.H;                                                \
+        const int grid = round_up(total, kXcds);                                            \
+        hipLaunchKernelGGL((score_select_kernel<D, J, T>), dim3(grid), dim3(64 * W), 0,     \
+                           stream, qbar, kbar, g, scale, tau, tiles, idx, cnt, totals);     \
+    } while (0)
+    if (jpl <= 1) SOL_SELECT_CASE(1, 16);
+    else if (jpl <= 2) SOL_SELECT_CASE(2, 16);
+    else if (jpl <= 4) SOL_SELECT_CASE(4, 8);
+    else SOL_SELECT_CASE(8, 4);
+#undef SOL_SELECT_CASE
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t route_ws_floats(const Geom& g) {
+    // qbar and kbar, each B * H * NB * D floats, each rounded to 64 floats
+    const size_t one = (size_t)g.B * g.H * g.NB * g.D;
+    return 2 * ((one + 63) / 64 * 64);
+}
+
+hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale, float tau,
+                        int16_t* idx, int32_t* cnt, int64_t* totals, float* ws,
+                        hipStream_t stream)
+{
+    if (g.ncand == 0) {
+        const int n = g.B * g.H * g.NB;
+        const long long pairs = (long long)g.B * g.H * g.N * g.Ssink;
+        hipLaunchKernelGGL(empty_route_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cnt, n,
+                           totals, pairs);
+        return hipGetLastError();
+    }
+    const size_t one = ((size_t)g.B * g.H * g.NB * g.D + 63) / 64 * 64;
+    float* qbar = ws;
+    float* kbar = ws + one;
+    const int lanes = g.H * (g.D / 8);
+    dim3 grid(g.NB, (lanes + 255) / 256, g.B * 2);
+    hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, stream, (const uint16_t*)q,
+                       (const uint16_t*)k, g, qbar, kbar, totals);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (g.D == 128) return launch_select<128>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream);
+    return launch_select<64>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream);
+}
+
+}  // namespace sol

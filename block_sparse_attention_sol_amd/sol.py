@@ -1,0 +1,165 @@
+"""Thin ctypes binding of libsol.so (C ABI in include/sol.h).
+
+Argument marshalling only: every step of routing and attention runs in the
+HIP kernels of libsol.  PyTorch provides device memory and the current
+stream.  Importing this module fails loudly when libsol.so has not been built
+(``python -m block_sparse_attention_sol_amd.build``); there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsol.so")
+
+BLOCK = 64
+
+SOL_OK, SOL_ERR_ARG, SOL_ERR_UNSUPPORTED, SOL_ERR_ALIGN, SOL_ERR_WORKSPACE, SOL_ERR_HIP = range(6)
+
+
+class SolError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("N", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("D", ctypes.c_int32),
+                ("qkv_sb", ctypes.c_int64), ("qkv_sn", ctypes.c_int64), ("qkv_sh", ctypes.c_int64),
+                ("o_sb", ctypes.c_int64), ("o_sn", ctypes.c_int64), ("o_sh", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libsol.so not built at {_LIB_PATH}; run "
+                          "`python -m block_sparse_attention_sol_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    dp = ctypes.POINTER(Desc)
+    lib.sol_num_blocks.argtypes, lib.sol_num_blocks.restype = [i32], i32
+    lib.sol_route_workspace_bytes.argtypes, lib.sol_route_workspace_bytes.restype = [dp], sz
+    lib.sol_route.argtypes = [vp, vp, dp, f32, i32, f32, vp, vp, vp, vp, sz, vp]
+    lib.sol_route.restype = ctypes.c_int
+    lib.sol_attn_fwd.argtypes = [vp, vp, vp, dp, vp, vp, i32, f32, vp, vp, vp]
+    lib.sol_attn_fwd.restype = ctypes.c_int
+    lib.sol_attn_dense_fwd.argtypes = [vp, vp, vp, dp, f32, vp, vp, vp]
+    lib.sol_attn_dense_fwd.restype = ctypes.c_int
+    lib.sol_status_str.argtypes, lib.sol_status_str.restype = [ctypes.c_int], ctypes.c_char_p
+    _ = i64
+    return lib
+
+
+lib = _load()
+
+
+def status_str(status: int) -> str:
+    return lib.sol_status_str(int(status)).decode()
+
+
+def num_blocks(N: int) -> int:
+    return int(lib.sol_num_blocks(int(N)))
+
+
+def _check(status: int, what: str) -> None:
+    if status != SOL_OK:
+        raise SolError(status, what)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def make_desc(q: torch.Tensor, o: torch.Tensor | None = None) -> Desc:
+    """Descriptor of [B, N, H, D] bf16 tensors: Q/K/V strides from q, O strides from o."""
+    if q.dim() != 4:
+        raise ValueError("expected [B, N, H, D] tensors")
+    B, N, H, D = q.shape
+    o = q if o is None else o
+    if q.stride(3) != 1 or o.stride(3) != 1:
+        raise SolError(SOL_ERR_UNSUPPORTED, "stride along D must be 1")
+    return Desc(B, N, H, D, q.stride(0), q.stride(1), q.stride(2), o.stride(0), o.stride(1), o.stride(2))
+
+
+def _check_qkv(q, k, v=None):
+    ts = [q, k] + ([v] if v is not None else [])
+    for t in ts:
+        if not t.is_cuda or t.dtype != torch.bfloat16:
+            raise ValueError("Q, K, V must be bf16 CUDA(HIP) tensors")
+        if t.shape != q.shape or t.stride() != q.stride():
+            raise ValueError("Q, K, V must share shape and strides")
+
+
+def route_workspace_bytes(q: torch.Tensor) -> int:
+    return int(lib.sol_route_workspace_bytes(ctypes.byref(make_desc(q))))
+
+
+def route_outputs(q: torch.Tensor):
+    """Empty (blk_idx, blk_cnt, totals) tensors for route() on q's shape."""
+    B, N, H, D = q.shape
+    NB = num_blocks(N)
+    return (torch.empty((B, H, NB, NB), dtype=torch.int16, device=q.device),
+            torch.empty((B, H, NB), dtype=torch.int32, device=q.device),
+            torch.empty(2, dtype=torch.int64, device=q.device))
+
+
+def route(q: torch.Tensor, k: torch.Tensor, tau: float, sink: int, scale: float = 0.0,
+          workspace: torch.Tensor | None = None, out=None):
+    """Online block routing.  Returns (blk_idx int16 [B,H,NB,NB], blk_cnt int32 [B,H,NB],
+    totals int64 [2]) on q's device; only the first blk_cnt entries of each row are set."""
+    _check_qkv(q, k)
+    desc = make_desc(q)
+    idx, cnt, totals = route_outputs(q) if out is None else out
+    need = int(lib.sol_route_workspace_bytes(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.sol_route(q.data_ptr(), k.data_ptr(), ctypes.byref(desc), ctypes.c_float(tau),
+                       int(sink), ctypes.c_float(scale), idx.data_ptr(), cnt.data_ptr(),
+                       totals.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q))
+    _check(st, "sol_route")
+    return idx, cnt, totals
+
+
+def attn(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, out=None, return_lse=False):
+    """Sink + routed block-sparse attention forward.  Returns O (and LSE [B,H,N] fp32)."""
+    _check_qkv(q, k, v)
+    B, N, H, D = q.shape
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    if blk_idx.dtype != torch.int16 or blk_cnt.dtype != torch.int32:
+        raise ValueError("blk_idx must be int16 and blk_cnt int32")
+    st = lib.sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(make_desc(q, o)),
+                          blk_idx.data_ptr(), blk_cnt.data_ptr(), int(sink), ctypes.c_float(scale),
+                          o.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q))
+    _check(st, "sol_attn_fwd")
+    return (o, lse) if return_lse else o
+
+
+def attn_dense(q, k, v, scale: float = 0.0, out=None, return_lse=False):
+    """Full softmax attention (routing disabled)."""
+    _check_qkv(q, k, v)
+    B, N, H, D = q.shape
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib.sol_attn_dense_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                ctypes.byref(make_desc(q, o)), ctypes.c_float(scale), o.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, _stream(q))
+    _check(st, "sol_attn_dense_fwd")
+    return (o, lse) if return_lse else o
+
+
+def forward(q, k, v, tau: float, sink: int, scale: float = 0.0, return_lse=False):
+    """Routing then sparse attention on the current stream; returns (O, [LSE,] idx, cnt, totals)."""
+    idx, cnt, totals = route(q, k, tau, sink, scale)
+    res = attn(q, k, v, idx, cnt, sink, scale, return_lse=return_lse)
+    if return_lse:
+        return res[0], res[1], idx, cnt, totals
+    return res, idx, cnt, totals
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

@@ -1,0 +1,153 @@
+/*
+ * sol.h -- C ABI of the MI355X (gfx950) Sol-Attn block-sparse attention forward.
+ *
+ * The forward has three parts, all described on the MiniMax-H3 acceleration
+ * pages (no page gives code or an API; the operations below are read from
+ * their prose):
+ *
+ *   routing   online, per head, from compressed queries and keys: every
+ *             64-token query block picks the key blocks it attends to, with
+ *             threshold tau and the diagonal block always kept (clawpit.io
+ *             article on the single-4090 run, paragraph on the Sol-Attn
+ *             settings; nvlabs.github.io Sol-Engine H3-DataCenter page,
+ *             policy paragraph "same online routing"; ty-yang3015 "MiniAcc"
+ *             post, "What is Sol attention?": a set of pairs per head).
+ *   sink      an exact dense prefix: every query attends to the first S keys
+ *             (nvlabs page, policy paragraph: exact 951-token multimodal
+ *             prefix sink).
+ *   attention softmax attention over the sink keys and the routed keys only,
+ *             the two parts merged exactly by log-sum-exp.
+ *
+ * Tokens form contiguous 64-token blocks in sequence order (nvlabs page: no
+ * token reordering).  N is a runtime argument and any N works with the one
+ * ahead-of-time build: padding to the 64-aligned length is logical only,
+ * padded keys carry exactly zero weight and padded rows are never read or
+ * written (tokenfactory.fast post, "The benchmark was not the product": a
+ * kernel keyed on the live token count paid a 12-14 s compile per prompt
+ * length; the fix was the 64-aligned length with padding masked to zero).
+ *
+ * Notation:  Blk = 64, NB = ceil(N / 64), scale = 1/sqrt(D) unless given.
+ *   j0   = S / 64 (integer division) when S < N, else NB: first key block
+ *          holding a non-sink key.  Candidates are the key blocks j0..NB-1.
+ *   R(j) = keys [max(64 j, S), min(64 j + 64, N)): the routable keys of block j.
+ *   Routing score of query block i and candidate j, float32 in a fixed order:
+ *          qbar_i = mean of rows [64 i, min(64 i + 64, N)) of Q   (rows added
+ *                   in ascending order from +0, then one correctly rounded divide)
+ *          kbar_j = mean of the rows R(j) of K                     (same order)
+ *          s_ij   = (fma chain over d = 0..D-1 ascending of qbar_i[d]*kbar_j[d],
+ *                   starting from +0) * scale
+ *   Selection:  T_i = float32(max_j s_ij - tau);  keep j iff s_ij >= T_i or
+ *          j == i.  The pages name tau and a "diagonal threshold" but print no
+ *          formula; this gap-to-the-maximum rule is the reading taken.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are device pointers owned by the caller; the library never
+ *     allocates or frees memory and keeps no per-call state.
+ *   - Q, K, V are [B, N, H, D] bf16 with element strides (sb, sn, sh) shared
+ *     by the three tensors (they may be views of one merged QKV projection)
+ *     and unit stride along D; O has its own strides.  Rows >= N are never
+ *     read (loads past them return zero) and never written.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronise the host.
+ *   - Errors come back as a status code; nothing is printed.  Argument checks
+ *     run on the host before any HIP call, so a rejected call touches no
+ *     device state.  SOL_ERR_HIP means a kernel launch failed.
+ *   - D must be 64 or 128.  Base pointers and strides must give 16-byte
+ *     aligned rows.
+ *   - Thread safety: calls on different streams may run concurrently; the
+ *     library has no mutable global state.
+ */
+#ifndef SOL_H
+#define SOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SOL_BLOCK 64
+
+typedef enum {
+    SOL_OK = 0,
+    SOL_ERR_ARG = 1,          /* null pointer, non-positive size, negative S, NaN or negative tau */
+    SOL_ERR_UNSUPPORTED = 2,  /* D not 64/128, stride along D != 1, a size beyond the limits    */
+    SOL_ERR_ALIGN = 3,        /* a pointer or stride that breaks 16-byte row alignment          */
+    SOL_ERR_WORKSPACE = 4,    /* workspace null or smaller than sol_route_workspace_bytes()     */
+    SOL_ERR_HIP = 5           /* a kernel launch reported an error                              */
+} sol_status;
+
+typedef struct {
+    int32_t B, N, H, D;               /* batch, true sequence length, heads, head width    */
+    int64_t qkv_sb, qkv_sn, qkv_sh;   /* element strides of Q, K and V (unit along D)      */
+    int64_t o_sb, o_sn, o_sh;         /* element strides of O (unit along D)               */
+} sol_desc;
+
+/* Number of 64-token blocks, ceil(N / 64) (0 for N <= 0). */
+int32_t sol_num_blocks(int32_t N);
+
+/* Device workspace that sol_route needs, in bytes: the pooled queries and
+ * keys, 2 * B * H * NB * D float32 plus alignment.  0 for an invalid desc. */
+size_t sol_route_workspace_bytes(const sol_desc* desc);
+
+/*
+ * sol_route -- online block routing (pooling, pooled scores, selection).
+ *
+ *   q, k      [B, N, H, D] bf16 device tensors (strides in desc).
+ *   tau       threshold >= 0 in scaled-logit units; +INFINITY keeps every
+ *             candidate (routing disabled).  NaN or negative: SOL_ERR_ARG.
+ *   sink_len  S >= 0; S = 0 disables the sink, S >= N makes every key a sink
+ *             key (no candidates, every list empty).
+ *   scale     softmax scale of the scores; 0 means 1/sqrt(D).
+ *   blk_idx   out, device int16 [B, H, NB, NB]: row (b, h, i) holds the
+ *             selected key blocks of query block i in ascending order in its
+ *             first blk_cnt[b, h, i] entries; the rest of the row is not
+ *             written.  Requires NB <= 32767.
+ *   blk_cnt   out, device int32 [B, H, NB].
+ *   totals    out, device int64 [2]: totals[0] = sum of blk_cnt (routed block
+ *             pairs); totals[1] = attended (query, key) pairs over valid rows,
+ *             sink included.  Exact integers, so densities are exact.
+ *   workspace device scratch of at least sol_route_workspace_bytes(desc)
+ *             bytes, 256-byte aligned; contents on entry are ignored.
+ *
+ * Limits: NB - j0 <= 4096 candidates (N up to about 262k tokens).
+ */
+sol_status sol_route(const void* q, const void* k, const sol_desc* desc, float tau,
+                     int32_t sink_len, float scale, int16_t* blk_idx, int32_t* blk_cnt,
+                     int64_t* totals, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sol_attn_fwd -- sink + routed block-sparse attention forward.
+ *
+ *   q, k, v   [B, N, H, D] bf16 device tensors (strides in desc).
+ *   blk_idx,  the lists written by sol_route for the same B, N, H and
+ *   blk_cnt   sink_len (entries must be ascending candidates in [j0, NB)).
+ *   sink_len  S >= 0 as for sol_route.
+ *   scale     softmax scale; 0 means 1/sqrt(D).
+ *   o         out, [B, N, H, D] bf16 (strides in desc): for each valid query
+ *             row, softmax attention over keys [0, min(S, N)) and the keys
+ *             R(j) of every listed block j, rounded to bf16 (nearest even).
+ *   lse       out, optional (NULL to skip), float32 [B, H, N]: natural-log
+ *             log-sum-exp of the scaled logits over the same keys.
+ */
+sol_status sol_attn_fwd(const void* q, const void* k, const void* v, const sol_desc* desc,
+                        const int16_t* blk_idx, const int32_t* blk_cnt, int32_t sink_len,
+                        float scale, void* o, float* lse, void* stream);
+
+/*
+ * sol_attn_dense_fwd -- full softmax attention (routing disabled), the path
+ * the pages keep for the first denoising steps and first layers (nvlabs page,
+ * policy paragraph).  Arguments as for sol_attn_fwd; every key is attended.
+ */
+sol_status sol_attn_dense_fwd(const void* q, const void* k, const void* v, const sol_desc* desc,
+                              float scale, void* o, float* lse, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* sol_status_str(sol_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOL_H */

@@ -1,0 +1,168 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/sol.h declares, and rejects bad arguments on the host before any HIP
+call.  Every case below breaks exactly one rule that is checked before a
+launch, so none of them reaches the device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sol.h")
+LIB = os.path.join(ROOT, "block_sparse_attention_sol_amd", "libsol.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from block_sparse_attention_sol_amd.build import build
+        build()
+    from block_sparse_attention_sol_amd import sol
+    return sol
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sol_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["sol_route", "sol_attn_fwd", "sol_attn_dense_fwd", "sol_status_str",
+              "sol_route_workspace_bytes", "sol_num_blocks"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert isinstance(lib.status_str(code), str) and lib.status_str(code)
+    assert lib.status_str(0) == "ok"
+    assert lib.status_str(99) == "unknown status"
+
+
+def test_num_blocks(lib):
+    assert lib.num_blocks(38247) == 598
+    assert lib.num_blocks(64) == 1 and lib.num_blocks(65) == 2 and lib.num_blocks(0) == 0
+
+
+def _desc(lib, B=1, N=1000, H=2, D=128, sn=None, sh=None, sb=None):
+    sh = D if sh is None else sh
+    sn = H * D if sn is None else sn
+    sb = N * sn if sb is None else sb
+    return lib.Desc(B, N, H, D, sb, sn, sh, sb, sn, sh)
+
+
+def _route(lib, desc, q=0x10000, k=0x20000, tau=1.0, sink=64, scale=0.0, idx=0x30000,
+           cnt=0x40000, tot=0x50000, ws=0x60000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return lib.lib.sol_route(q, k, ctypes.byref(desc), ctypes.c_float(tau), sink,
+                             ctypes.c_float(scale), idx, cnt, tot, ws, ws_bytes, None)
+
+
+def _attn(lib, desc, q=0x10000, k=0x20000, v=0x30000, idx=0x40000, cnt=0x50000, sink=64,
+          scale=0.0, o=0x60000, lse=None):
+    return lib.lib.sol_attn_fwd(q, k, v, ctypes.byref(desc), idx, cnt, sink, ctypes.c_float(scale),
+                                o, lse, None)
+
+
+def test_workspace_size(lib):
+    d = _desc(lib, N=38247, H=56)
+    assert lib.lib.sol_route_workspace_bytes(ctypes.byref(d)) >= 2 * 56 * 598 * 128 * 4
+    assert lib.lib.sol_route_workspace_bytes(ctypes.byref(_desc(lib, D=96))) == 0
+    assert lib.lib.sol_route_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_desc", 1), ("D96", 2), ("N0", 1), ("negative_sink", 1), ("null_q", 1),
+    ("nan_tau", 1), ("negative_tau", 1), ("nan_scale", 1), ("misaligned_q", 3),
+    ("odd_stride", 3), ("small_workspace", 4), ("null_workspace", 4), ("misaligned_ws", 3),
+    ("too_many_blocks", 2), ("huge_span", 2),
+])
+def test_route_argument_errors(lib, case, expect):
+    d = _desc(lib)
+    kw = {}
+    if case == "null_desc":
+        st = lib.lib.sol_route(0x10000, 0x20000, None, ctypes.c_float(1.0), 0, ctypes.c_float(0),
+                               0x30000, 0x40000, 0x50000, 0x60000, 1 << 30, None)
+        assert st == expect
+        return
+    if case == "D96":
+        d = _desc(lib, D=96)
+    elif case == "N0":
+        d = _desc(lib, N=0)
+    elif case == "negative_sink":
+        kw["sink"] = -1
+    elif case == "null_q":
+        kw["q"] = None
+    elif case == "nan_tau":
+        kw["tau"] = math.nan
+    elif case == "negative_tau":
+        kw["tau"] = -0.5
+    elif case == "nan_scale":
+        kw["scale"] = math.nan
+    elif case == "misaligned_q":
+        kw["q"] = 0x10008
+    elif case == "odd_stride":
+        d = _desc(lib, sn=2 * 128 + 4)
+    elif case == "small_workspace":
+        kw["ws_bytes"] = 100
+    elif case == "null_workspace":
+        kw["ws"] = None
+    elif case == "misaligned_ws":
+        kw["ws"] = 0x60010
+    elif case == "too_many_blocks":
+        d = _desc(lib, N=64 * 5000, H=1)          # 5000 candidate blocks > 4096
+    elif case == "huge_span":
+        d = _desc(lib, N=1 << 20, H=64, D=128)    # 32-bit per-head byte window exceeded
+    assert _route(lib, d, **kw) == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("D32", 2), ("null_v", 1), ("null_idx", 1), ("misaligned_o", 3), ("misaligned_lse", 3),
+    ("negative_scale", 1), ("inf_scale", 1), ("odd_o_stride", 3),
+])
+def test_attention_argument_errors(lib, case, expect):
+    d = _desc(lib)
+    kw = {}
+    if case == "D32":
+        d = _desc(lib, D=32)
+    elif case == "null_v":
+        kw["v"] = None
+    elif case == "null_idx":
+        kw["idx"] = None
+    elif case == "misaligned_o":
+        kw["o"] = 0x60002
+    elif case == "misaligned_lse":
+        kw["lse"] = 0x70001
+    elif case == "negative_scale":
+        kw["scale"] = -1.0
+    elif case == "inf_scale":
+        kw["scale"] = math.inf
+    elif case == "odd_o_stride":
+        d = lib.Desc(1, 1000, 2, 128, 256000, 256, 128, 256000, 260, 128)
+    assert _attn(lib, d, **kw) == expect
+
+
+def test_dense_argument_errors(lib):
+    d = _desc(lib, D=80)
+    st = lib.lib.sol_attn_dense_fwd(0x10000, 0x20000, 0x30000, ctypes.byref(d), ctypes.c_float(0),
+                                    0x40000, None, None)
+    assert st == 2
+    d = _desc(lib)
+    st = lib.lib.sol_attn_dense_fwd(0x10000, None, 0x30000, ctypes.byref(d), ctypes.c_float(0),
+                                    0x40000, None, None)
+    assert st == 1

@@ -1,0 +1,210 @@
+"""GPU attention parity: sol_attn_fwd / sol_attn_dense_fwd vs the float64 oracle.
+
+Tolerance (bf16 output vs float64): max-abs <= 1e-2 and L2-relative <= 5e-3
+over the valid rows compared.  Routing lists come from the GPU route, whose
+parity with the oracle is checked first in each test, so both sides attend to
+the same keys.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import oracle as orc
+from tests.helpers import (assert_close, bf16_tensor_to_f64, compare_masks, gpu_lists_to_mask,
+                           log, sample_blocks, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sol():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import block_sparse_attention_sol_amd as s
+    return s
+
+
+def _run(sol, w: synth.Workload, blocks=None, dense=False, tau=None):
+    """GPU route + attention on workload w, compared with the oracle on `blocks` (or all)."""
+    import torch
+    tau = w.tau if tau is None else tau
+    q_bits, k_bits, v_bits = synth.make_qkv(w)
+    q32, k32, v32 = (synth.bf16_bits_to_f32(x) for x in (q_bits, k_bits, v_bits))
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    if dense:
+        o, lse = sol.attn_dense(q, k, v, return_lse=True)
+        g = orc.geometry(w.N, w.N)
+        O, L = orc.dense_attention(q32, k32, v32, blocks=blocks)
+    else:
+        idx, cnt, totals = sol.route(q, k, tau, w.sink)
+        o, lse = sol.attn(q, k, v, idx, cnt, w.sink, return_lse=True)
+        r = orc.route(q32, k32, w.N, w.sink, tau)
+        g = r.geom
+        gsel = gpu_lists_to_mask(idx.cpu().numpy(), cnt.cpu().numpy(), g.NB)
+        compare_masks(gsel, r)
+        O, L = orc.attention(q32, k32, v32, r.sel, g, blocks=blocks)
+    torch.cuda.synchronize()
+    got = bf16_tensor_to_f64(o)
+    lse = lse.cpu().numpy().astype(np.float64)
+    rows = ~np.isnan(O[..., 0, 0])                 # [B, N]: rows the oracle computed
+    if blocks is None:
+        ref, gv = O, got
+        lref, lgot = L, lse
+    else:
+        ref, gv = [], []
+        lref, lgot = [], []
+        for b, h, i in blocks:
+            rr = g.q_rows(i)
+            ref.append(O[b, rr.start:rr.stop, h])
+            gv.append(got[b, rr.start:rr.stop, h])
+            lref.append(L[b, h, rr.start:rr.stop])
+            lgot.append(lse[b, h, rr.start:rr.stop])
+        ref, gv = np.concatenate(ref), np.concatenate(gv)
+        lref, lgot = np.concatenate(lref), np.concatenate(lgot)
+    _ = rows
+    e = assert_close(gv, ref, f"{w.name} O")
+    lerr = float(np.abs(lgot - lref).max())
+    log(f"{w.name} LSE max-abs {lerr:.3e}")
+    assert lerr <= 2e-3
+    return e
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_attention_parity_small_configs_all_rows(sol, name):
+    w = synth.WORKLOADS[name]
+    log(f"attention parity {name} (all rows)")
+    _run(sol, w)
+
+
+def test_attention_parity_page_shape_sampled(sol):
+    w = synth.WORKLOADS["page"]
+    g = orc.geometry(w.N, w.sink)
+    blocks = sample_blocks(g, w.B, w.H, 40, seed=1)
+    log(f"attention parity page, {len(blocks)} sampled query blocks")
+    _run(sol, w, blocks=blocks)
+
+
+def test_dense_parity_page_shape_sampled(sol):
+    w = synth.WORKLOADS["page_dense"]
+    g = orc.geometry(w.N, w.N)
+    blocks = sample_blocks(g, w.B, w.H, 12, seed=2)
+    log(f"dense parity page, {len(blocks)} sampled query blocks")
+    _run(sol, w, blocks=blocks, dense=True)
+
+
+def test_attention_parity_varlen_sampled(sol):
+    for w in synth.varlen_calls()[:2]:
+        g = orc.geometry(w.N, w.sink)
+        blocks = sample_blocks(g, w.B, w.H, 16, seed=w.seed)
+        log(f"attention parity {w.name} N={w.N}")
+        _run(sol, w, blocks=blocks)
+
+
+EDGE = [
+    # B, N, H, D, S, tau
+    (1, 1, 1, 64, 0, 1.0),
+    (1, 37, 2, 128, 0, 0.5),
+    (2, 64, 1, 64, 0, 0.0),
+    (1, 65, 3, 128, 1, 0.3),
+    (1, 129, 1, 64, 64, 0.0),
+    (2, 300, 2, 128, 63, 0.7),
+    (1, 300, 2, 64, 65, 0.7),
+    (1, 1000, 3, 128, 951, 0.4),
+    (1, 700, 2, 128, 5000, 1.0),
+    (1, 2047, 2, 128, 130, math.inf),
+]
+
+
+@pytest.mark.parametrize("B,N,H,D,S,tau", EDGE)
+def test_attention_parity_edge_shapes(sol, B, N, H, D, S, tau):
+    log(f"attention edge B={B} N={N} H={H} D={D} S={S} tau={tau}")
+    w = synth.Workload("edge", B=B, N=N, H=H, D=D, sink=S, tau=tau, kind="field", alpha=1.0,
+                       seed=N + S)
+    _run(sol, w)
+
+
+@pytest.mark.parametrize("N,D", [(1, 64), (200, 128), (1000, 64), (3001, 128)])
+def test_dense_parity_edge_shapes(sol, N, D):
+    w = synth.Workload("dense_edge", B=1, N=N, H=2, D=D, sink=0, tau=math.inf, kind="field",
+                       alpha=1.0, seed=N)
+    _run(sol, w, dense=True)
+
+
+def test_density_one_sparse_equals_dense_bitwise(sol):
+    import torch
+    w = replace(synth.WORKLOADS["mid"], N=4000, H=4)
+    q_bits, k_bits, v_bits = synth.make_qkv(w)
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    idx, cnt, _ = sol.route(q, k, math.inf, w.sink)
+    o1 = sol.attn(q, k, v, idx, cnt, w.sink)
+    o2 = sol.attn_dense(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_padding_rows_contribute_exactly_zero(sol):
+    """Rows past N hold NaN or 0 in a 64-aligned allocation: outputs bit-identical."""
+    import torch
+    w = replace(synth.WORKLOADS["mid"], N=3000 + 17, H=3)
+    Np = 64 * sol.num_blocks(w.N)
+    q_bits, k_bits, v_bits = synth.make_qkv(w)
+    outs = []
+    for fill in (0.0, float("nan")):
+        bufs = []
+        for bits in (q_bits, k_bits, v_bits):
+            t = torch.full((w.B, Np, w.H, w.D), fill, dtype=torch.bfloat16, device="cuda")
+            t[:, : w.N] = to_dev(bits)
+            bufs.append(t[:, : w.N])
+        q, k, v = bufs
+        idx, cnt, tot = sol.route(q, k, w.tau, w.sink)
+        o_full = torch.full((w.B, Np, w.H, w.D), fill, dtype=torch.bfloat16, device="cuda")
+        o = sol.attn(q, k, v, idx, cnt, w.sink, out=o_full[:, : w.N])
+        od = sol.attn_dense(q, k, v)
+        torch.cuda.synchronize()
+        outs.append((o.clone(), od.clone(), cnt.clone(), tot.clone(), o_full[:, w.N:].clone()))
+    (a, ad, ca, ta, pa), (b, bd, cb, tb, pb) = outs
+    assert torch.isfinite(a.float()).all() and torch.isfinite(ad.float()).all()
+    assert torch.equal(a, b) and torch.equal(ad, bd) and torch.equal(ca, cb) and torch.equal(ta, tb)
+    # rows past N are never written
+    assert (pa.float() == 0).all() and torch.isnan(pb.float()).all()
+
+
+def test_constant_values_and_zero_queries(sol):
+    import torch
+    w = replace(synth.WORKLOADS["mid"], N=2000, H=2)
+    q_bits, k_bits, v_bits = synth.make_qkv(w)
+    q, k = to_dev(q_bits), to_dev(k_bits)
+    idx, cnt, _ = sol.route(q, k, w.tau, w.sink)
+    v = torch.full_like(q, 0.375)
+    o = sol.attn(q, k, v, idx, cnt, w.sink)
+    torch.cuda.synchronize()
+    assert (o.float() - 0.375).abs().max().item() <= 1e-2
+    # Q = 0: the mean of the attended values (oracle closed form)
+    vz = to_dev(v_bits)
+    oz = sol.attn(torch.zeros_like(q), k, vz, idx, cnt, w.sink)
+    torch.cuda.synchronize()
+    r = orc.route(synth.bf16_bits_to_f32(q_bits), synth.bf16_bits_to_f32(k_bits), w.N, w.sink, w.tau)
+    O, _ = orc.attention(np.zeros((w.B, w.N, w.H, w.D), np.float32), synth.bf16_bits_to_f32(k_bits),
+                         synth.bf16_bits_to_f32(v_bits), r.sel, r.geom)
+    assert_close(bf16_tensor_to_f64(oz), O, "zero queries")
+
+
+def test_strided_qkv_views_and_output(sol):
+    import torch
+    w = replace(synth.WORKLOADS["mid"], N=2500, H=4)
+    q_bits, k_bits, v_bits = synth.make_qkv(w)
+    qkv = torch.stack([to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)], dim=2)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    idx, cnt, _ = sol.route(q, k, w.tau, w.sink)
+    obuf = torch.zeros((w.B, w.N, w.H, 2 * w.D), dtype=torch.bfloat16, device="cuda")
+    o = sol.attn(q, k, v, idx, cnt, w.sink, out=obuf[..., : w.D])
+    ref = sol.attn(to_dev(q_bits), to_dev(k_bits), to_dev(v_bits), idx, cnt, w.sink)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
+    assert (obuf[..., w.D:].float() == 0).all()
