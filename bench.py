@@ -49,14 +49,14 @@ def measured_traffic(launch_bytes: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q_bits, k_bits, v_bits, n_blocks: int, flop_eff: float):
+def cpu_baseline(w, q_bits, k_bits, v_bits, n_heads: int, n_blocks: int, flop_eff: float):
     """Time the oracle (as it stands) on a bounded sample of the same workload."""
     import numpy as np
 
     import synth
     from oracle import oracle as orc
 
-    heads = [0, 1]
+    heads = list(range(n_heads))
     qh, kh, vh = (synth.bf16_bits_to_f32(x[:, :, heads]) for x in (q_bits, k_bits, v_bits))
     t0 = time.perf_counter()
     r = orc.route(qh, kh, w.N, w.sink, w.tau)
@@ -100,7 +100,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="page", choices=["page", "page_dense", "mid"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=48)
+    ap.add_argument("--cpu-blocks", type=int, default=2048)
+    ap.add_argument("--cpu-heads", type=int, default=4)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -229,7 +230,8 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         t0 = time.perf_counter()
-        rec["cpu_baseline"] = cpu_baseline(w, q_bits, k_bits, v_bits, args.cpu_blocks, flop_eff)
+        rec["cpu_baseline"] = cpu_baseline(w, q_bits, k_bits, v_bits, args.cpu_heads, args.cpu_blocks,
+                                           flop_eff)
         err(f"cpu baseline took {time.perf_counter() - t0:.1f} s")
     print(json.dumps(rec), flush=True)
     return 0
