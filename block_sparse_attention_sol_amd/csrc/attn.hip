@@ -71,6 +71,8 @@ __device__ __forceinline__ int vchunk(int key, int c) {
     return c ^ ((key * 4) & (Tile<D>::CHUNKS - 1));
 }
 
+constexpr int kMaxList = 4096;   // routed blocks per query block (candidate limit)
+
 template <int D, bool DENSE>
 __global__ __launch_bounds__(64) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -79,8 +81,11 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
     float* __restrict__ lse)
 {
     using T = Tile<D>;
-    __shared__ __attribute__((aligned(1024))) char vbuf0[64 * T::ROWB];
-    __shared__ __attribute__((aligned(1024))) char vbuf1[64 * T::ROWB];
+    constexpr int HALF_BYTES = 32 * T::ROWB;         // one 32-key half tile of V
+    constexpr int VH = HALF_BYTES / 1024;             // 16-byte loads per lane per half tile
+    constexpr int rows_per_load = 1024 / T::ROWB;
+    __shared__ __attribute__((aligned(1024))) char vbuf[2][HALF_BYTES];
+    __shared__ __attribute__((aligned(16))) int16_t lst[DENSE ? 8 : kMaxList];
 
     const int work = xcd_remap(blockIdx.x, gridDim.x, g.B * g.H * g.NB);
     if (work < 0) return;
@@ -106,38 +111,29 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
         for (int kc = 0; kc < T::KC; ++kc) qop[rt][kc] = load16(rq, base + 16 * kc);
     }
 
-    // ---- the tile walk: sink tiles, then routed blocks
+    // ---- the tile walk: sink tiles, then routed blocks (list copied to LDS)
     const int nsink = DENSE ? g.NB : (g.Ssink + 63) / 64;
     int nlist = 0, first = 0;
     bool straddle_in = false;
-    __amdgpu_buffer_rsrc_t rl = rq;
     if (!DENSE) {
-        nlist = min(max(cnt[work], 0), g.ncand);
-        rl = rsrc(idx + (int64_t)work * g.NB, (uint32_t)nlist * 2);
-    }
-    // list entries, 64 at a time: lane l holds entry 64 c + l (0 past the end)
-    auto list_chunk = [&](int c) -> int {
-        return (int)(int16_t)__builtin_amdgcn_raw_buffer_load_b16(rl, (uint32_t)(128 * c + 2 * lane), 0, 0);
-    };
-    int chunk_id = 0;
-    int chunk = 0;
-    if (!DENSE && nlist > 0) {
-        chunk = list_chunk(0);
-        if ((g.S & 63) != 0 && g.S < g.N && __builtin_amdgcn_readlane(chunk, 0) == g.j0) {
-            straddle_in = true;
-            first = 1;
+        nlist = min(max(cnt[work], 0), min(g.ncand, kMaxList));
+        if (nlist > 0) {
+            // 2-byte loads: buffer range checks work per dword, so a wider load
+            // would drop the last entry of an odd-length list
+            const __amdgpu_buffer_rsrc_t rl = rsrc(idx + (int64_t)work * g.NB, (uint32_t)nlist * 2);
+            for (int base = 0; base < nlist; base += 64)
+                lst[base + lane] = (int16_t)__builtin_amdgcn_raw_buffer_load_b16(
+                    rl, (uint32_t)(2 * (base + lane)), 0, 0);
+            if ((g.S & 63) != 0 && g.S < g.N && lst[0] == g.j0) {
+                straddle_in = true;
+                first = 1;
+            }
         }
     }
     const int ntiles = nsink + nlist - first;
-    // block of tile t (t must be the current or the next tile)
     auto tile_block = [&](int t) -> int {
         if (DENSE || t < nsink) return t;
-        const int e = first + t - nsink;
-        if ((e >> 6) != chunk_id) {
-            chunk_id = e >> 6;
-            chunk = list_chunk(chunk_id);
-        }
-        return min(max(__builtin_amdgcn_readlane(chunk, e & 63), 0), g.NB - 1);
+        return min(max((int)lst[first + t - nsink], 0), g.NB - 1);
     };
     auto tile_kmax = [&](int t, int blk) -> int {
         if (DENSE || t >= nsink) return min(64 * blk + 64, g.N);
@@ -145,20 +141,24 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
         return straddle_in ? min(64 * blk + 64, g.N) : g.Ssink;
     };
 
-    // V tile -> LDS by direct loads.  Load n, lane l writes LDS bytes
-    // [n * 1024 + 16 l, +16): tile row n * rows_per_load + l / CHUNKS, physical
-    // chunk l % CHUNKS.  The row swizzle only depends on the row modulo
-    // CHUNKS / 4, which is lane-constant here, so each load needs one VGPR
-    // offset per tile plus an SGPR step.
-    constexpr int rows_per_load = 1024 / T::ROWB;
+    // V half tile: global -> registers -> LDS.  Load n, lane l covers LDS
+    // bytes [n * 1024 + 16 l, +16): half-tile row n * rows_per_load + l / CHUNKS,
+    // physical chunk l % CHUNKS.  The row swizzle depends on the row modulo
+    // CHUNKS / 4 only, which is lane-constant, so one VGPR offset per half
+    // tile plus an SGPR step per load.
     const int vrow = lane / T::CHUNKS;
     const uint32_t v_lane = (uint32_t)vrow * rowstride + 16 * vchunk<D>(vrow, lane % T::CHUNKS);
-    auto issue_v = [&](int blk, char* buf) {
-        const uint32_t voff = v_lane + (uint32_t)(64 * blk) * rowstride;
+    uint4 vreg[VH];
+    auto load_v = [&](int blk, int kt) {
+        const uint32_t voff = v_lane + (uint32_t)(64 * blk + 32 * kt) * rowstride;
 #pragma unroll
-        for (int n = 0; n < T::VLOADS; ++n)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(buf + n * 1024), 16, voff,
-                                                     (uint32_t)(n * rows_per_load) * rowstride, 0, 0);
+        for (int n = 0; n < VH; ++n)
+            vreg[n] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                rv, voff, (uint32_t)(n * rows_per_load) * rowstride, 0));
+    };
+    auto store_v = [&](char* buf) {
+#pragma unroll
+        for (int n = 0; n < VH; ++n) *(uint4*)(buf + n * 1024 + 16 * lane) = vreg[n];
     };
     // K operand of one 32-key half tile: lane holds key l32, channels u*D/2 ..
     bf16x8 kop[T::KC];
@@ -169,8 +169,8 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
         for (int kc = 0; kc < T::KC; ++kc)
             kop[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 16 * kc, 0, 0));
     };
-    // transposed-read offsets: row cb + 8 half + 4 u + (lane & 15) / 4 of the
-    // tile, channels 32 dt + 16 ((lane >> 4) & 1) + 4 (lane & 3)
+    // transposed-read offsets in a half-tile buffer: row 16 c2 + 8 half + 4 u +
+    // (lane & 15) / 4, channels 32 dt + 16 ((lane >> 4) & 1) + 4 (lane & 3)
     uint32_t v_rd[T::DT];
     {
         const int key = 4 * u + ((lane & 15) >> 2);
@@ -182,21 +182,53 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
     }
 
     f32x16 oacc[T::DT][2];
-#pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) oacc[dt][rt] = f32x16{};
-    // mref: per-row reference maximum (log2 units) of the accumulation.  It is
-    // fixed by the first half tile and only moved, with O and l rescaled, when
-    // a later score exceeds it by more than kRescaleSlack; in between,
-    // exp2 values stay below 2^kRescaleSlack.  O and l always share mref, so
-    // the final O / l is exact whatever mref is.
+    // mref: per-row reference maximum (log2 units) of the accumulation, taken
+    // from the first half tile.  Scores may exceed it by up to kRescaleSlack
+    // (exp2 values then stay below 2^kRescaleSlack).  If one exceeds it by
+    // more, the walk restarts from scratch with the larger reference; O and l
+    // always share mref, so the final O / l is exact whatever mref is.  The
+    // restart keeps O out of any VALU read-modify-write inside the loop nest.
     float mref[2] = {-INFINITY, -INFINITY};
     float lsum[2] = {0.f, 0.f};
 
-    // softmax of one 32-key half tile against mref, then O^T += V^T P^T
-    auto finish_half = [&](f32x16 (&s)[2], int kt, const char* cur, bool more) {
-        bf16x8 p[2][2];   // [c2][rt]
+    // S^T = K Q^T for the 32 keys whose K sits in kop: lane holds rows
+    // 32 rt + l32 and keys 8 (r/4) + 4 u + r%4 of the half tile.
+    auto mfma_s = [&](f32x16 (&s)[2]) {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < T::KC; ++kc)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+                s[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kc], qop[rt][kc], s[rt], 0, 0, 0);
+    };
+    // keys >= kmax of the half tile at kbase get -inf; row maxima in score units
+    auto mask_max = [&](f32x16 (&s)[2], int kbase, int kmax, float (&mx)[2]) {
+        if (kmax < kbase + 32) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kbase + 8 * (r / 4) + 4 * u + (r & 3);
+                if (key >= kmax) {
+                    s[0][r] = -INFINITY;
+                    s[1][r] = -INFINITY;
+                }
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            float m = fmaxf(s[rt][0], s[rt][1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(s[rt][r], s[rt][r + 1]));
+            mx[rt] = fmaxf(m, __shfl_xor(m, 32, 64));
+        }
+    };
+    auto needs_rescale = [&](const float (&mx)[2]) -> bool {
+        const bool need = (mx[0] * scale_log2 > mref[0] + kRescaleSlack) ||
+                          (mx[1] * scale_log2 > mref[1] + kRescaleSlack);
+        return __builtin_amdgcn_ballot_w64(need) != 0;
+    };
+    // p = exp2(s * scale_log2 - mref) as bf16 B operands [c2][rt]; l += sum p
+    auto softmax = [&](f32x16 (&s)[2], bf16x8 (&p)[2][2]) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const float nm = -mref[rt];
@@ -216,115 +248,110 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
                 p[c2][rt] = __builtin_convertvector(h8, bf16x8);
             }
         }
-        if (kt == 0) {
-            // V(t) must have landed in LDS: wait for all but the loads issued
-            // after it (V(t+1) when there is a next tile, and one K half)
-            if (more) {
-                constexpr int pending = T::VLOADS + T::KC;
-                __builtin_amdgcn_s_waitcnt((pending & 15) | ((pending >> 4) << 14) | (7 << 4) | (15 << 8));
-            } else {
-                constexpr int pending = T::KC;
-                __builtin_amdgcn_s_waitcnt((pending & 15) | ((pending >> 4) << 14) | (7 << 4) | (15 << 8));
-            }
-        }
+    };
+    // O^T += V^T P^T over the 32 keys held in the half-tile buffer `cur`
+    auto pv = [&](bf16x8 (&p)[2][2], const char* cur) {
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
-            const int cb = 32 * kt + 16 * c2;
+            bf16x8 vop[T::DT];
 #pragma unroll
-            for (int dt = 0; dt < T::DT; ++dt) {
-                bf16x8 vop;
+            for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    // rows cb + 8 half keep the row modulo 4, so the swizzle holds
+                    // rows 16 c2 + 8 half keep the row modulo 4, so the swizzle holds
                     const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4*)(cur + v_rd[dt] + (cb + 8 * half) * T::ROWB));
+                        (lds_s16x4*)(cur + v_rd[dt] + (16 * c2 + 8 * half) * T::ROWB));
                     const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) vop[4 * half + e] = xb[e];
+                    for (int e = 0; e < 4; ++e) vop[dt][4 * half + e] = xb[e];
                 }
 #pragma unroll
+            for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
-                    oacc[dt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, p[c2][rt], oacc[dt][rt], 0, 0, 0);
+                    oacc[dt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[dt], p[c2][rt],
+                                                                           oacc[dt][rt], 0, 0, 0);
+        }
+    };
+
+    // One 32-key half step h = (t, kt).  On entry s_cur holds the masked scores
+    // of step h and mx_cur their row maxima, kop holds K of step h + 1, vreg
+    // holds V of step h + 1 (in flight) and vbuf[kt] holds V of step h.  The S
+    // MFMAs of step h + 1 run under this step's softmax, and the masking and
+    // maxima of step h + 1 run under this step's P V MFMAs.
+    int blk = 0, nblk = 0;
+    auto half_step = [&](int t, int kt, f32x16 (&s_cur)[2], f32x16 (&s_next)[2],
+                         float (&mx_next)[2]) {
+        const bool more = t + 1 < ntiles;
+        if (kt == 0) nblk = more ? tile_block(t + 1) : 0;
+        // V of step h + 1 into the other buffer, then fetch V of step h + 2
+        if (kt == 0 || more) store_v(vbuf[kt ^ 1]);
+        if (more) load_v(nblk, kt);
+        bf16x8 p[2][2];
+        mfma_s(s_next);          // harmless extra work after the last step
+        softmax(s_cur, p);
+#pragma unroll
+        for (int i = 0; i < T::KC * 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        if (more) load_k(nblk, kt);
+        pv(p, vbuf[kt]);
+        if (kt == 0) mask_max(s_next, 64 * blk + 32, tile_kmax(t, blk), mx_next);
+        else mask_max(s_next, 64 * nblk, tile_kmax(t + 1, nblk), mx_next);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::DT, 1);
+#pragma unroll
+            for (int i = 0; i < T::DT * 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
             }
         }
     };
 
-    // walk in 32-key half tiles; step = 2 t + kt
-    const int nsteps = 2 * ntiles;
-    int blk = ntiles > 0 ? tile_block(0) : 0;
-    int nblk = 0;
-    if (ntiles > 0) {
-        issue_v(blk, vbuf0);
+    f32x16 sA[2], sB[2];
+    float mxA[2] = {0.f, 0.f}, mxB[2] = {0.f, 0.f};
+    for (int pass = 0;; ++pass) {
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) oacc[dt][rt] = f32x16{};
+        lsum[0] = 0.f;
+        lsum[1] = 0.f;
+        if (ntiles == 0) break;
+        blk = tile_block(0);
+        load_v(blk, 0);
         load_k(blk, 0);
-    }
-    int step = 0;
-    f32x16 s[2];
-    float mnew[2];
-    while (step < nsteps) {
-        bool rescale = false;
-        for (; step < nsteps; ++step) {
-            const int t = step >> 1, kt = step & 1;
-            const bool more = t + 1 < ntiles;
-            if (kt == 0) {
-                nblk = more ? tile_block(t + 1) : 0;
-                if (more) issue_v(nblk, (t & 1) ? vbuf0 : vbuf1);
-            }
-            // S^T = K Q^T for 32 keys: lane holds rows 32 rt + l32, keys 8 (r/4) + 4 u + r%4
-            s[0] = f32x16{};
-            s[1] = f32x16{};
-#pragma unroll
-            for (int kc = 0; kc < T::KC; ++kc)
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-                    s[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kc], qop[rt][kc], s[rt], 0, 0, 0);
-            if (kt == 0) load_k(blk, 1);
-            else if (more) load_k(nblk, 0);
-
-            const int kmax = tile_kmax(t, blk);
-            const int kbase = 64 * blk + 32 * kt;
-            if (kmax < kbase + 32) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kbase + 8 * (r / 4) + 4 * u + (r & 3);
-                    if (key >= kmax) {
-                        s[0][r] = -INFINITY;
-                        s[1][r] = -INFINITY;
-                    }
-                }
-            }
-            bool need = false;
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                float mx = s[rt][0];
-#pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[rt][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                mnew[rt] = mx * scale_log2;
-                need |= mnew[rt] > mref[rt] + kRescaleSlack;
-            }
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                rescale = true;
+        store_v(vbuf[0]);
+        load_v(blk, 1);
+        mfma_s(sA);
+        load_k(blk, 1);
+        mask_max(sA, 64 * blk, tile_kmax(0, blk), mxA);
+        if (pass == 0) {
+            // every tile holds at least one valid key, so this is finite
+            mref[0] = mxA[0] * scale_log2;
+            mref[1] = mxA[1] * scale_log2;
+        }
+        bool restart = false;
+        for (int t = 0; t < ntiles; ++t) {
+            if (needs_rescale(mxA)) {
+                restart = true;
+                mref[0] = fmaxf(mref[0], mxA[0] * scale_log2);
+                mref[1] = fmaxf(mref[1], mxA[1] * scale_log2);
                 break;
             }
-            finish_half(s, kt, (t & 1) ? vbuf1 : vbuf0, more);
-            if (kt == 1) blk = nblk;
-        }
-        if (rescale) {
-            // rare: a score above mref + slack (always at the first half tile)
-            const int t = step >> 1, kt = step & 1;
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const float m_use = fmaxf(mref[rt], mnew[rt]);
-                const float alpha = __builtin_amdgcn_exp2f(mref[rt] - m_use);
-                mref[rt] = m_use;
-                lsum[rt] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < T::DT; ++dt) oacc[dt][rt] *= alpha;
+            half_step(t, 0, sA, sB, mxB);
+            if (needs_rescale(mxB)) {
+                restart = true;
+                mref[0] = fmaxf(mref[0], mxB[0] * scale_log2);
+                mref[1] = fmaxf(mref[1], mxB[1] * scale_log2);
+                break;
             }
-            finish_half(s, kt, (t & 1) ? vbuf1 : vbuf0, t + 1 < ntiles);
-            if (kt == 1) blk = nblk;
-            ++step;
+            half_step(t, 1, sB, sA, mxA);
+            blk = nblk;
         }
+        if (!restart) break;
     }
     const float* mrow = mref;
 
