@@ -102,6 +102,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2048)
     ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 5 times (for scaling "
+                         "the HBM counters FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -112,6 +115,16 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        err(f"copied {args.copy_calibration} bytes 5 times")
+        return 0
 
     import block_sparse_attention_sol_amd as sol
     import synth

@@ -32,6 +32,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -110,6 +111,12 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
 #pragma unroll
         for (int kc = 0; kc < T::KC; ++kc) qop[rt][kc] = load16(rq, base + 16 * kc);
     }
+    // Q is only ever an MFMA source: keep it in AGPRs, which MFMA reads
+    // directly, and leave the VGPRs to the scores and the accumulator
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int kc = 0; kc < T::KC; ++kc) asm volatile("" : "+a"(qop[rt][kc]));
 
     // ---- the tile walk: sink tiles, then routed blocks (list copied to LDS)
     const int nsink = DENSE ? g.NB : (g.Ssink + 63) / 64;
@@ -148,26 +155,28 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
     // tile plus an SGPR step per load.
     const int vrow = lane / T::CHUNKS;
     const uint32_t v_lane = (uint32_t)vrow * rowstride + 16 * vchunk<D>(vrow, lane % T::CHUNKS);
-    uint4 vreg[VH];
-    auto load_v = [&](int blk, int kt) {
+    // Two register sets each for V and K (half step h uses set h % 2), so
+    // both are fetched two half steps ahead of their use.
+    uint4 vreg[2][VH];
+    auto load_v = [&](int set, int blk, int kt) {
         const uint32_t voff = v_lane + (uint32_t)(64 * blk + 32 * kt) * rowstride;
 #pragma unroll
         for (int n = 0; n < VH; ++n)
-            vreg[n] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            vreg[set][n] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 rv, voff, (uint32_t)(n * rows_per_load) * rowstride, 0));
     };
-    auto store_v = [&](char* buf) {
+    auto store_v = [&](int set, char* buf) {
 #pragma unroll
-        for (int n = 0; n < VH; ++n) *(uint4*)(buf + n * 1024 + 16 * lane) = vreg[n];
+        for (int n = 0; n < VH; ++n) *(uint4*)(buf + n * 1024 + 16 * lane) = vreg[set][n];
     };
     // K operand of one 32-key half tile: lane holds key l32, channels u*D/2 ..
-    bf16x8 kop[T::KC];
+    bf16x8 kop[2][T::KC];
     const uint32_t k_lane = (uint32_t)l32 * rowstride + u * D;
-    auto load_k = [&](int blk, int kt) {
+    auto load_k = [&](int set, int blk, int kt) {
         const uint32_t voff = k_lane + (uint32_t)(64 * blk + 32 * kt) * rowstride;
 #pragma unroll
         for (int kc = 0; kc < T::KC; ++kc)
-            kop[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 16 * kc, 0, 0));
+            kop[set][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 16 * kc, 0, 0));
     };
     // transposed-read offsets in a half-tile buffer: row 16 c2 + 8 half + 4 u +
     // (lane & 15) / 4, channels 32 dt + 16 ((lane >> 4) & 1) + 4 (lane & 3)
@@ -193,14 +202,14 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
 
     // S^T = K Q^T for the 32 keys whose K sits in kop: lane holds rows
     // 32 rt + l32 and keys 8 (r/4) + 4 u + r%4 of the half tile.
-    auto mfma_s = [&](f32x16 (&s)[2]) {
+    auto mfma_s = [&](int set, f32x16 (&s)[2]) {
         s[0] = f32x16{};
         s[1] = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < T::KC; ++kc)
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
-                s[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kc], qop[rt][kc], s[rt], 0, 0, 0);
+                s[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[set][kc], qop[rt][kc], s[rt], 0, 0, 0);
     };
     // keys >= kmax of the half tile at kbase get -inf; row maxima in score units
     auto mask_max = [&](f32x16 (&s)[2], int kbase, int kmax, float (&mx)[2]) {
@@ -227,33 +236,34 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
                           (mx[1] * scale_log2 > mref[1] + kRescaleSlack);
         return __builtin_amdgcn_ballot_w64(need) != 0;
     };
-    // p = exp2(s * scale_log2 - mref) as bf16 B operands [c2][rt]; l += sum p
-    auto softmax = [&](f32x16 (&s)[2], bf16x8 (&p)[2][2]) {
+    // Row tile rt: p = exp2(s * scale_log2 - mref) as bf16 B operands p[c2][rt];
+    // l += sum of the bf16 p (v_dot2 with ones: two keys per instruction, and
+    // the same rounded weights that multiply V)
+    auto softmax_rt = [&](f32x16 (&s)[2], bf16x8 (&p)[2][2], int rt) {
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        const float nm = -mref[rt];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const float nm = -mref[rt];
-            float acc = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][r], scale_log2, nm));
-                s[rt][r] = e;
-                acc += e;
-            }
-            lsum[rt] += acc;
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                f32x8 h8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) h8[e] = s[rt][8 * c2 + e];
-                p[c2][rt] = __builtin_convertvector(h8, bf16x8);
-            }
-        }
-    };
-    // O^T += V^T P^T over the 32 keys held in the half-tile buffer `cur`
-    auto pv = [&](bf16x8 (&p)[2][2], const char* cur) {
+        for (int r = 0; r < 16; ++r)
+            s[rt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][r], scale_log2, nm));
+        float acc = lsum[rt];
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
-            bf16x8 vop[T::DT];
+            f32x8 h8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h8[e] = s[rt][8 * c2 + e];
+            p[c2][rt] = __builtin_convertvector(h8, bf16x8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16x2 pr = {p[c2][rt][2 * e], p[c2][rt][2 * e + 1]};
+                acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+            }
+        }
+        lsum[rt] = acc;
+    };
+    // V^T operands of the 32 keys held in the half-tile buffer `cur`
+    auto read_v = [&](const char* cur, bf16x8 (&vop)[2][T::DT]) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
             for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
@@ -263,50 +273,69 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
                         (lds_s16x4*)(cur + v_rd[dt] + (16 * c2 + 8 * half) * T::ROWB));
                     const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) vop[dt][4 * half + e] = xb[e];
+                    for (int e = 0; e < 4; ++e) vop[c2][dt][4 * half + e] = xb[e];
                 }
+    };
+    // O^T += V^T P^T for row tile rt over those 32 keys
+    auto pv_rt = [&](bf16x8 (&p)[2][2], bf16x8 (&vop)[2][T::DT], int rt) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
             for (int dt = 0; dt < T::DT; ++dt)
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-                    oacc[dt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[dt], p[c2][rt],
-                                                                           oacc[dt][rt], 0, 0, 0);
-        }
+                oacc[dt][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c2][dt], p[c2][rt],
+                                                                       oacc[dt][rt], 0, 0, 0);
     };
 
     // One 32-key half step h = (t, kt).  On entry s_cur holds the masked scores
-    // of step h and mx_cur their row maxima, kop holds K of step h + 1, vreg
-    // holds V of step h + 1 (in flight) and vbuf[kt] holds V of step h.  The S
-    // MFMAs of step h + 1 run under this step's softmax, and the masking and
-    // maxima of step h + 1 run under this step's P V MFMAs.
-    int blk = 0, nblk = 0;
+    // of step h and mx_cur their row maxima; register set (h + 1) % 2 holds K
+    // of step h + 1 and V of step h + 1 (both may still be in flight), set
+    // h % 2 holds K and V of step h + 2 in flight, and vbuf[kt] holds V of
+    // step h.  The S MFMAs of step h + 1 run under this step's softmax, and
+    // the masking and maxima of step h + 1 run under this step's P V MFMAs.
+    // blk, nblk, nnblk: key blocks of tiles t, t + 1, t + 2 (past the end
+    // they repeat a valid block: the prefetches then re-read it, harmlessly,
+    // and loads issued on every path keep the compiler's wait counts exact).
+    int blk = 0, nblk = 0, nnblk = 0;
     auto half_step = [&](int t, int kt, f32x16 (&s_cur)[2], f32x16 (&s_next)[2],
                          float (&mx_next)[2]) {
-        const bool more = t + 1 < ntiles;
-        if (kt == 0) nblk = more ? tile_block(t + 1) : 0;
-        // V of step h + 1 into the other buffer, then fetch V of step h + 2
-        if (kt == 0 || more) store_v(vbuf[kt ^ 1]);
-        if (more) load_v(nblk, kt);
+        const int nxt = kt ^ 1;           // register set of steps h + 1 and h + 3
+        // step h + 3 is (t + 1, 1) when kt = 0 and (t + 2, 0) when kt = 1
+        const int blk3 = kt == 0 ? nblk : nnblk;
+        // ---- one straight-line scheduling region: the MFMA stream runs
+        // S(h+1) then P V(h) back to back while the VALU does softmax(h)
+        store_v(nxt, vbuf[nxt]);          // V of step h + 1
+        load_v(nxt, blk3, kt ^ 1);        // V of step h + 3
+        mfma_s(nxt, s_next);              // harmless extra work after the last step
+        load_k(nxt, blk3, kt ^ 1);        // K of step h + 3
         bf16x8 p[2][2];
-        mfma_s(s_next);          // harmless extra work after the last step
-        softmax(s_cur, p);
+        bf16x8 vop[2][T::DT];
+        softmax_rt(s_cur, p, 0);
+        read_v(vbuf[kt], vop);
+        pv_rt(p, vop, 0);
+        softmax_rt(s_cur, p, 1);
+        pv_rt(p, vop, 1);
+        __builtin_amdgcn_sched_group_barrier(0x200, VH, 0);        // V stores
+        __builtin_amdgcn_sched_group_barrier(0x020, VH, 0);        // V loads
 #pragma unroll
-        for (int i = 0; i < T::KC * 2; ++i) {
+        for (int i = 0; i < 2 * T::KC; ++i) {                      // S MFMAs | softmax rt 0
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         }
-        if (more) load_k(nblk, kt);
-        pv(p, vbuf[kt]);
-        if (kt == 0) mask_max(s_next, 64 * blk + 32, tile_kmax(t, blk), mx_next);
-        else mask_max(s_next, 64 * nblk, tile_kmax(t + 1, nblk), mx_next);
+        __builtin_amdgcn_sched_group_barrier(0x020, T::KC, 0);     // K loads
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * T::DT, 0); // V^T reads
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::DT, 1);
-#pragma unroll
-            for (int i = 0; i < T::DT * 2; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);
-            }
+        for (int i = 0; i < 2 * T::DT; ++i) {                      // P V rt 0 | softmax rt 1
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::DT, 0); // P V rt 1
+        // ---- after the region (runs under the last MFMAs): the next step's
+        // mask and maxima, and the list entry of tile t + 2
+        if (kt == 0) {
+            nnblk = (t + 2 < ntiles) ? tile_block(t + 2) : nblk;
+            mask_max(s_next, 64 * blk + 32, tile_kmax(t, blk), mx_next);
+        } else {
+            mask_max(s_next, 64 * nblk, tile_kmax(t + 1, nblk), mx_next);
         }
     };
 
@@ -321,12 +350,16 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
         lsum[1] = 0.f;
         if (ntiles == 0) break;
         blk = tile_block(0);
-        load_v(blk, 0);
-        load_k(blk, 0);
-        store_v(vbuf[0]);
-        load_v(blk, 1);
-        mfma_s(sA);
-        load_k(blk, 1);
+        nblk = ntiles > 1 ? tile_block(1) : blk;
+        // steps 0, 1, 2 = (0, 0), (0, 1), (1, 0)
+        load_v(0, blk, 0);
+        load_k(0, blk, 0);
+        load_v(1, blk, 1);
+        load_k(1, blk, 1);
+        store_v(0, vbuf[0]);
+        load_v(0, nblk, 0);
+        mfma_s(0, sA);
+        load_k(0, nblk, 0);
         mask_max(sA, 64 * blk, tile_kmax(0, blk), mxA);
         if (pass == 0) {
             // every tile holds at least one valid key, so this is finite
@@ -350,6 +383,7 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
             }
             half_step(t, 1, sB, sA, mxA);
             blk = nblk;
+            nblk = nnblk;
         }
         if (!restart) break;
     }
