@@ -1,7 +1,8 @@
 """Ahead-of-time build of libsol.so for gfx950 with hipcc (in-tree).
 
 One build serves every sequence length: N, B and H are runtime arguments.
-Run as ``python -m block_sparse_attention_sol_amd.build``.
+Run as ``python block_sparse_attention_sol_amd/build.py`` (by path: importing the
+package loads the library this script builds).
 """
 
 from __future__ import annotations

@@ -3,7 +3,7 @@
 Argument marshalling only: every step of routing and attention runs in the
 HIP kernels of libsol.  PyTorch provides device memory and the current
 stream.  Importing this module fails loudly when libsol.so has not been built
-(``python -m block_sparse_attention_sol_amd.build``); there is no fallback.
+(``python block_sparse_attention_sol_amd/build.py``); there is no fallback.
 """
 
 from __future__ import annotations
@@ -37,7 +37,7 @@ class Desc(ctypes.Structure):
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"libsol.so not built at {_LIB_PATH}; run "
-                          "`python -m block_sparse_attention_sol_amd.build` (hipcc, gfx950)")
+                          "`python block_sparse_attention_sol_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     dp = ctypes.POINTER(Desc)

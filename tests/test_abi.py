@@ -21,8 +21,8 @@ LIB = os.path.join(ROOT, "block_sparse_attention_sol_amd", "libsol.so")
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from block_sparse_attention_sol_amd.build import build
-        build()
+        import __graft_entry__
+        __graft_entry__.build()
     from block_sparse_attention_sol_amd import sol
     return sol
 
