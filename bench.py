@@ -143,14 +143,14 @@ def main() -> int:
     o = torch.empty_like(q)
     ws = torch.empty(max(sol.route_workspace_bytes(q), 256), dtype=torch.uint8, device=dev)
     outs = sol.route_outputs(q)
-    idx, cnt, totals = outs
+    idx, cnt, totals, order = outs
 
     def step():
         if dense:
             sol.attn_dense(q, k, v, out=o)
         else:
             sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs)
-            sol.attn(q, k, v, idx, cnt, w.sink, out=o)
+            sol.attn(q, k, v, idx, cnt, w.sink, out=o, order=order)
 
     for _ in range(args.warmup):
         step()
@@ -170,7 +170,7 @@ def main() -> int:
         if dense:
             sol.attn_dense(q, k, v, out=o)
         else:
-            sol.attn(q, k, v, idx, cnt, w.sink, out=o)
+            sol.attn(q, k, v, idx, cnt, w.sink, out=o, order=order)
         ev[s][2].record()
     end.record()
     torch.cuda.synchronize()

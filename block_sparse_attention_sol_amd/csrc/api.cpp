@@ -70,7 +70,8 @@ size_t sol_route_workspace_bytes(const sol_desc* desc) {
 
 sol_status sol_route(const void* q, const void* k, const sol_desc* desc, float tau,
                      int32_t sink_len, float scale, int16_t* blk_idx, int32_t* blk_cnt,
-                     int64_t* totals, void* workspace, size_t ws_bytes, void* stream) {
+                     int64_t* totals, int32_t* order, void* workspace, size_t ws_bytes,
+                     void* stream) {
     sol::Geom g;
     const sol_status st = check_desc(desc, sink_len, &g);
     if (st != SOL_OK) return st;
@@ -79,21 +80,23 @@ sol_status sol_route(const void* q, const void* k, const sol_desc* desc, float t
     if (std::isnan(tau) || tau < 0.0f || std::isnan(scale) || scale < 0.0f || std::isinf(scale))
         return SOL_ERR_ARG;
     if (!aligned16(q) || !aligned16(k) || (reinterpret_cast<uintptr_t>(totals) & 7u) != 0 ||
-        (reinterpret_cast<uintptr_t>(blk_cnt) & 3u) != 0 || (reinterpret_cast<uintptr_t>(blk_idx) & 1u) != 0)
+        (reinterpret_cast<uintptr_t>(blk_cnt) & 3u) != 0 || (reinterpret_cast<uintptr_t>(blk_idx) & 1u) != 0 ||
+        (reinterpret_cast<uintptr_t>(order) & 3u) != 0)
         return SOL_ERR_ALIGN;
     if (g.NB > 32767 || g.ncand > kMaxCandidates) return SOL_ERR_UNSUPPORTED;
     const size_t need = sol::route_ws_floats(g) * sizeof(float);
     if (workspace == nullptr || ws_bytes < need) return SOL_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SOL_ERR_ALIGN;
     const hipError_t e = sol::launch_route(g, q, k, resolve_scale(scale, g.D), tau, blk_idx, blk_cnt,
-                                           totals, static_cast<float*>(workspace),
+                                           totals, order, static_cast<float*>(workspace),
                                            static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SOL_OK : SOL_ERR_HIP;
 }
 
 static sol_status attn_common(const void* q, const void* k, const void* v, const sol_desc* desc,
-                              const int16_t* blk_idx, const int32_t* blk_cnt, int32_t sink_len,
-                              float scale, void* o, float* lse, bool dense, void* stream) {
+                              const int16_t* blk_idx, const int32_t* blk_cnt, const int32_t* order,
+                              int32_t sink_len, float scale, void* o, float* lse, bool dense,
+                              void* stream) {
     sol::Geom g;
     const sol_status st = check_desc(desc, dense ? desc ? desc->N : 0 : sink_len, &g);
     if (st != SOL_OK) return st;
@@ -104,23 +107,26 @@ static sol_status attn_common(const void* q, const void* k, const void* v, const
         (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
         return SOL_ERR_ALIGN;
     if (!dense && ((reinterpret_cast<uintptr_t>(blk_cnt) & 3u) != 0 ||
-                   (reinterpret_cast<uintptr_t>(blk_idx) & 1u) != 0))
+                   (reinterpret_cast<uintptr_t>(blk_idx) & 1u) != 0 ||
+                   (reinterpret_cast<uintptr_t>(order) & 3u) != 0))
         return SOL_ERR_ALIGN;
     if (!dense && (g.NB > 32767 || g.ncand > kMaxCandidates)) return SOL_ERR_UNSUPPORTED;
-    const hipError_t e = sol::launch_attn(g, q, k, v, blk_idx, blk_cnt, resolve_scale(scale, g.D), o,
-                                          lse, dense, static_cast<hipStream_t>(stream));
+    const hipError_t e = sol::launch_attn(g, q, k, v, blk_idx, blk_cnt, dense ? nullptr : order,
+                                          resolve_scale(scale, g.D), o, lse, dense,
+                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SOL_OK : SOL_ERR_HIP;
 }
 
 sol_status sol_attn_fwd(const void* q, const void* k, const void* v, const sol_desc* desc,
-                        const int16_t* blk_idx, const int32_t* blk_cnt, int32_t sink_len,
-                        float scale, void* o, float* lse, void* stream) {
-    return attn_common(q, k, v, desc, blk_idx, blk_cnt, sink_len, scale, o, lse, false, stream);
+                        const int16_t* blk_idx, const int32_t* blk_cnt, const int32_t* order,
+                        int32_t sink_len, float scale, void* o, float* lse, void* stream) {
+    return attn_common(q, k, v, desc, blk_idx, blk_cnt, order, sink_len, scale, o, lse, false,
+                       stream);
 }
 
 sol_status sol_attn_dense_fwd(const void* q, const void* k, const void* v, const sol_desc* desc,
                               float scale, void* o, float* lse, void* stream) {
-    return attn_common(q, k, v, desc, nullptr, nullptr, 0, scale, o, lse, true, stream);
+    return attn_common(q, k, v, desc, nullptr, nullptr, nullptr, 0, scale, o, lse, true, stream);
 }
 
 const char* sol_status_str(sol_status status) {

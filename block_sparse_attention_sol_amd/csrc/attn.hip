@@ -78,20 +78,28 @@ template <int D, bool DENSE>
 __global__ __launch_bounds__(64) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, Geom g, const int16_t* __restrict__ idx,
-    const int32_t* __restrict__ cnt, float scale_log2, uint16_t* __restrict__ o,
-    float* __restrict__ lse)
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ order, float scale_log2,
+    uint16_t* __restrict__ o, float* __restrict__ lse)
 {
     using T = Tile<D>;
     constexpr int HALF_BYTES = 32 * T::ROWB;         // one 32-key half tile of V
     constexpr int VH = HALF_BYTES / 1024;             // 16-byte loads per lane per half tile
     constexpr int rows_per_load = 1024 / T::ROWB;
     __shared__ __attribute__((aligned(1024))) char vbuf[2][HALF_BYTES];
-    __shared__ __attribute__((aligned(16))) int16_t lst[DENSE ? 8 : kMaxList];
+    // routed list of this query block: round_up(min(ncand, kMaxList), 64)
+    // entries of dynamic LDS (sized at launch, so short sequences keep the
+    // footprint small and more waves fit on a CU)
+    extern __shared__ __attribute__((aligned(16))) int16_t lst[];
 
     const int work = xcd_remap(blockIdx.x, gridDim.x, g.B * g.H * g.NB);
     if (work < 0) return;
     const int bh = work / g.NB;
-    const int qb = work - bh * g.NB;
+    // the rank-th query block of this (batch, head) in the routing schedule
+    // (longest list first), or in sequence order without one
+    const int rank = work - bh * g.NB;
+    const int qb = (DENSE || order == nullptr)
+                       ? rank : min(max(order[(int64_t)bh * g.NB + rank], 0), g.NB - 1);
+    const int item = bh * g.NB + qb;
     const int b = bh / g.H, h = bh - b * g.H;
     const int lane = threadIdx.x;
     const int l32 = lane & 31, u = lane >> 5;
@@ -123,11 +131,11 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
     int nlist = 0, first = 0;
     bool straddle_in = false;
     if (!DENSE) {
-        nlist = min(max(cnt[work], 0), min(g.ncand, kMaxList));
+        nlist = min(max(cnt[item], 0), min(g.ncand, kMaxList));
         if (nlist > 0) {
             // 2-byte loads: buffer range checks work per dword, so a wider load
             // would drop the last entry of an odd-length list
-            const __amdgpu_buffer_rsrc_t rl = rsrc(idx + (int64_t)work * g.NB, (uint32_t)nlist * 2);
+            const __amdgpu_buffer_rsrc_t rl = rsrc(idx + (int64_t)item * g.NB, (uint32_t)nlist * 2);
             for (int base = 0; base < nlist; base += 64)
                 lst[base + lane] = (int16_t)__builtin_amdgcn_raw_buffer_load_b16(
                     rl, (uint32_t)(2 * (base + lane)), 0, 0);
@@ -421,29 +429,30 @@ __global__ __launch_bounds__(64) void attn_fwd_kernel(
 
 template <int D, bool DENSE>
 hipError_t launch(const Geom& g, const void* q, const void* k, const void* v,
-                  const int16_t* idx, const int32_t* cnt, float scale, void* o, float* lse,
-                  hipStream_t stream)
+                  const int16_t* idx, const int32_t* cnt, const int32_t* order, float scale,
+                  void* o, float* lse, hipStream_t stream)
 {
     const int total = g.B * g.H * g.NB;
     const int grid = round_up(total, kXcds);
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE>), dim3(grid), dim3(64), 0, stream,
+    const size_t lds_list = DENSE ? 0 : (size_t)round_up(min(g.ncand, kMaxList), 64) * sizeof(int16_t);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE>), dim3(grid), dim3(64), lds_list, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, g, idx, cnt,
-                       scale_log2, (uint16_t*)o, lse);
+                       order, scale_log2, (uint16_t*)o, lse);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn(const Geom& g, const void* q, const void* k, const void* v,
-                       const int16_t* idx, const int32_t* cnt, float scale, void* o,
-                       float* lse, bool dense, hipStream_t stream)
+                       const int16_t* idx, const int32_t* cnt, const int32_t* order, float scale,
+                       void* o, float* lse, bool dense, hipStream_t stream)
 {
     if (g.D == 128)
-        return dense ? launch<128, true>(g, q, k, v, idx, cnt, scale, o, lse, stream)
-                     : launch<128, false>(g, q, k, v, idx, cnt, scale, o, lse, stream);
-    return dense ? launch<64, true>(g, q, k, v, idx, cnt, scale, o, lse, stream)
-                 : launch<64, false>(g, q, k, v, idx, cnt, scale, o, lse, stream);
+        return dense ? launch<128, true>(g, q, k, v, idx, cnt, order, scale, o, lse, stream)
+                     : launch<128, false>(g, q, k, v, idx, cnt, order, scale, o, lse, stream);
+    return dense ? launch<64, true>(g, q, k, v, idx, cnt, order, scale, o, lse, stream)
+                 : launch<64, false>(g, q, k, v, idx, cnt, order, scale, o, lse, stream);
 }
 
 }  // namespace sol

@@ -221,16 +221,68 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
         atomicAdd((unsigned long long*)&totals[1], (unsigned long long)keys_local);
 }
 
-// S >= N: no candidates, every list is empty, only sink pairs are attended.
-__global__ __launch_bounds__(256) void empty_route_kernel(int32_t* __restrict__ cnt, int n,
+// S >= N: no candidates, every list is empty, only sink pairs are attended;
+// the schedule is sequence order.
+__global__ __launch_bounds__(256) void empty_route_kernel(int32_t* __restrict__ cnt, int n, int NB,
                                                           int64_t* __restrict__ totals,
-                                                          long long sink_pairs)
+                                                          long long sink_pairs,
+                                                          int32_t* __restrict__ order)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) cnt[i] = 0;
+    if (i < n) {
+        cnt[i] = 0;
+        if (order != nullptr) order[i] = i % NB;
+    }
     if (i == 0) {
         totals[0] = 0;
         totals[1] = sink_pairs;
+    }
+}
+
+// Attention schedule: the query blocks of each (batch, head) sorted by list
+// length, longest first (a counting sort over the lengths 0..ncand).  Running
+// the long walks first balances the tail of the attention launch, and query
+// blocks running side by side then have lists of similar length, so their
+// ascending walks sweep the key blocks at similar rates and share them in L2.
+// Blocks of equal length keep no particular order; each query block's output
+// does not depend on the order, only the timing does.
+// grid: B * H; block: 256; dynamic LDS: ncand + 1 ints.
+__global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ cnt, Geom g,
+                                                    int32_t* __restrict__ order)
+{
+    extern __shared__ int hist[];          // per list length: count, then next slot
+    __shared__ int part[256];
+    const int tid = threadIdx.x;
+    const int nbins = g.ncand + 1;
+    const int64_t row = (int64_t)blockIdx.x * g.NB;
+    for (int b = tid; b < nbins; b += 256) hist[b] = 0;
+    __syncthreads();
+    for (int i = tid; i < g.NB; i += 256) atomicAdd(&hist[min(max(cnt[row + i], 0), g.ncand)], 1);
+    __syncthreads();
+    // descending exclusive scan: thread t owns lengths ncand - k for k in its range
+    const int per = (nbins + 255) / 256;
+    const int k0 = min(tid * per, nbins), k1 = min(k0 + per, nbins);
+    int local = 0;
+    for (int kk = k0; kk < k1; ++kk) local += hist[g.ncand - kk];
+    part[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {      // inclusive Hillis-Steele scan
+        const int add = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += add;
+        __syncthreads();
+    }
+    int run = part[tid] - local;
+    for (int kk = k0; kk < k1; ++kk) {
+        const int b = g.ncand - kk;
+        const int n = hist[b];
+        hist[b] = run;
+        run += n;
+    }
+    __syncthreads();
+    for (int i = tid; i < g.NB; i += 256) {
+        const int pos = atomicAdd(&hist[min(max(cnt[row + i], 0), g.ncand)], 1);
+        order[row + pos] = i;
     }
 }
 
@@ -266,14 +318,14 @@ size_t route_ws_floats(const Geom& g) {
 }
 
 hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale, float tau,
-                        int16_t* idx, int32_t* cnt, int64_t* totals, float* ws,
+                        int16_t* idx, int32_t* cnt, int64_t* totals, int32_t* order, float* ws,
                         hipStream_t stream)
 {
     if (g.ncand == 0) {
         const int n = g.B * g.H * g.NB;
         const long long pairs = (long long)g.B * g.H * g.N * g.Ssink;
         hipLaunchKernelGGL(empty_route_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cnt, n,
-                           totals, pairs);
+                           g.NB, totals, pairs, order);
         return hipGetLastError();
     }
     const size_t one = ((size_t)g.B * g.H * g.NB * g.D + 63) / 64 * 64;
@@ -285,8 +337,12 @@ hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale
                        (const uint16_t*)k, g, qbar, kbar, totals);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (g.D == 128) return launch_select<128>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream);
-    return launch_select<64>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream);
+    e = g.D == 128 ? launch_select<128>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream)
+                   : launch_select<64>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream);
+    if (e != hipSuccess || order == nullptr) return e;
+    hipLaunchKernelGGL(order_kernel, dim3(g.B * g.H), dim3(256), (size_t)(g.ncand + 1) * sizeof(int),
+                       stream, cnt, g, order);
+    return hipGetLastError();
 }
 
 }  // namespace sol

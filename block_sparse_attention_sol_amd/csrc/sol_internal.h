@@ -33,15 +33,16 @@ __device__ __forceinline__ int xcd_remap(int wg, int grid, int total) {
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-// Routing launch: pool + score/select.  ws holds qbar then kbar.
+// Routing launch: pool + score/select (+ schedule when order != nullptr).
+// ws holds qbar then kbar.
 hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale, float tau,
-                        int16_t* idx, int32_t* cnt, int64_t* totals, float* ws,
+                        int16_t* idx, int32_t* cnt, int64_t* totals, int32_t* order, float* ws,
                         hipStream_t stream);
 size_t route_ws_floats(const Geom& g);
 
-// Attention launches.
+// Attention launches; order (nullable) is the routing schedule.
 hipError_t launch_attn(const Geom& g, const void* q, const void* k, const void* v,
-                       const int16_t* idx, const int32_t* cnt, float scale, void* o,
-                       float* lse, bool dense, hipStream_t stream);
+                       const int16_t* idx, const int32_t* cnt, const int32_t* order, float scale,
+                       void* o, float* lse, bool dense, hipStream_t stream);
 
 }  // namespace sol

@@ -43,9 +43,9 @@ def _load():
     dp = ctypes.POINTER(Desc)
     lib.sol_num_blocks.argtypes, lib.sol_num_blocks.restype = [i32], i32
     lib.sol_route_workspace_bytes.argtypes, lib.sol_route_workspace_bytes.restype = [dp], sz
-    lib.sol_route.argtypes = [vp, vp, dp, f32, i32, f32, vp, vp, vp, vp, sz, vp]
+    lib.sol_route.argtypes = [vp, vp, dp, f32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     lib.sol_route.restype = ctypes.c_int
-    lib.sol_attn_fwd.argtypes = [vp, vp, vp, dp, vp, vp, i32, f32, vp, vp, vp]
+    lib.sol_attn_fwd.argtypes = [vp, vp, vp, dp, vp, vp, vp, i32, f32, vp, vp, vp]
     lib.sol_attn_fwd.restype = ctypes.c_int
     lib.sol_attn_dense_fwd.argtypes = [vp, vp, vp, dp, f32, vp, vp, vp]
     lib.sol_attn_dense_fwd.restype = ctypes.c_int
@@ -99,41 +99,50 @@ def route_workspace_bytes(q: torch.Tensor) -> int:
 
 
 def route_outputs(q: torch.Tensor):
-    """Empty (blk_idx, blk_cnt, totals) tensors for route() on q's shape."""
+    """Empty (blk_idx, blk_cnt, totals, order) tensors for route() on q's shape."""
     B, N, H, D = q.shape
     NB = num_blocks(N)
     return (torch.empty((B, H, NB, NB), dtype=torch.int16, device=q.device),
             torch.empty((B, H, NB), dtype=torch.int32, device=q.device),
-            torch.empty(2, dtype=torch.int64, device=q.device))
+            torch.empty(2, dtype=torch.int64, device=q.device),
+            torch.empty((B, H, NB), dtype=torch.int32, device=q.device))
 
 
 def route(q: torch.Tensor, k: torch.Tensor, tau: float, sink: int, scale: float = 0.0,
           workspace: torch.Tensor | None = None, out=None):
     """Online block routing.  Returns (blk_idx int16 [B,H,NB,NB], blk_cnt int32 [B,H,NB],
-    totals int64 [2]) on q's device; only the first blk_cnt entries of each row are set."""
+    totals int64 [2], order int32 [B,H,NB]) on q's device; only the first blk_cnt entries
+    of each row of blk_idx are set; order is the attention schedule (longest list first)."""
     _check_qkv(q, k)
     desc = make_desc(q)
-    idx, cnt, totals = route_outputs(q) if out is None else out
+    idx, cnt, totals, order = route_outputs(q) if out is None else out
     need = int(lib.sol_route_workspace_bytes(ctypes.byref(desc)))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     st = lib.sol_route(q.data_ptr(), k.data_ptr(), ctypes.byref(desc), ctypes.c_float(tau),
                        int(sink), ctypes.c_float(scale), idx.data_ptr(), cnt.data_ptr(),
-                       totals.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q))
+                       totals.data_ptr(), order.data_ptr() if order is not None else None,
+                       workspace.data_ptr(), workspace.numel(), _stream(q))
     _check(st, "sol_route")
-    return idx, cnt, totals
+    return idx, cnt, totals, order
 
 
-def attn(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, out=None, return_lse=False):
-    """Sink + routed block-sparse attention forward.  Returns O (and LSE [B,H,N] fp32)."""
+def attn(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, out=None, return_lse=False,
+         order=None):
+    """Sink + routed block-sparse attention forward.  Returns O (and LSE [B,H,N] fp32).
+    ``order`` is the schedule from route() (None: sequence order; results are the same)."""
     _check_qkv(q, k, v)
     B, N, H, D = q.shape
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
     if blk_idx.dtype != torch.int16 or blk_cnt.dtype != torch.int32:
         raise ValueError("blk_idx must be int16 and blk_cnt int32")
+    if order is not None and (order.dtype != torch.int32 or order.shape != blk_cnt.shape):
+        raise ValueError("order must be int32 with blk_cnt's shape")
     st = lib.sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(make_desc(q, o)),
-                          blk_idx.data_ptr(), blk_cnt.data_ptr(), int(sink), ctypes.c_float(scale),
+                          blk_idx.data_ptr(), blk_cnt.data_ptr(),
+                          order.data_ptr() if order is not None else None, int(sink),
+                          ctypes.c_float(scale),
                           o.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q))
     _check(st, "sol_attn_fwd")
     return (o, lse) if return_lse else o
@@ -154,8 +163,8 @@ def attn_dense(q, k, v, scale: float = 0.0, out=None, return_lse=False):
 
 def forward(q, k, v, tau: float, sink: int, scale: float = 0.0, return_lse=False):
     """Routing then sparse attention on the current stream; returns (O, [LSE,] idx, cnt, totals)."""
-    idx, cnt, totals = route(q, k, tau, sink, scale)
-    res = attn(q, k, v, idx, cnt, sink, scale, return_lse=return_lse)
+    idx, cnt, totals, order = route(q, k, tau, sink, scale)
+    res = attn(q, k, v, idx, cnt, sink, scale, return_lse=return_lse, order=order)
     if return_lse:
         return res[0], res[1], idx, cnt, totals
     return res, idx, cnt, totals

@@ -108,6 +108,11 @@ size_t sol_route_workspace_bytes(const sol_desc* desc);
  *   totals    out, device int64 [2]: totals[0] = sum of blk_cnt (routed block
  *             pairs); totals[1] = attended (query, key) pairs over valid rows,
  *             sink included.  Exact integers, so densities are exact.
+ *   order     out, optional (NULL to skip), device int32 [B, H, NB]: the
+ *             attention schedule.  Row (b, h) is a permutation of the query
+ *             blocks 0..NB-1 with non-increasing blk_cnt (longest list first;
+ *             blocks of equal length in no fixed order).  It changes only the
+ *             timing of sol_attn_fwd, never its results.
  *   workspace device scratch of at least sol_route_workspace_bytes(desc)
  *             bytes, 256-byte aligned; contents on entry are ignored.
  *
@@ -115,7 +120,8 @@ size_t sol_route_workspace_bytes(const sol_desc* desc);
  */
 sol_status sol_route(const void* q, const void* k, const sol_desc* desc, float tau,
                      int32_t sink_len, float scale, int16_t* blk_idx, int32_t* blk_cnt,
-                     int64_t* totals, void* workspace, size_t ws_bytes, void* stream);
+                     int64_t* totals, int32_t* order, void* workspace, size_t ws_bytes,
+                     void* stream);
 
 /*
  * sol_attn_fwd -- sink + routed block-sparse attention forward.
@@ -123,6 +129,10 @@ sol_status sol_route(const void* q, const void* k, const sol_desc* desc, float t
  *   q, k, v   [B, N, H, D] bf16 device tensors (strides in desc).
  *   blk_idx,  the lists written by sol_route for the same B, N, H and
  *   blk_cnt   sink_len (entries must be ascending candidates in [j0, NB)).
+ *   order     optional (NULL: sequence order) schedule written by sol_route;
+ *             each row must be a permutation of 0..NB-1.  Query blocks of one
+ *             (batch, head) are processed in this order; results do not
+ *             depend on it.
  *   sink_len  S >= 0 as for sol_route.
  *   scale     softmax scale; 0 means 1/sqrt(D).
  *   o         out, [B, N, H, D] bf16 (strides in desc): for each valid query
@@ -132,8 +142,8 @@ sol_status sol_route(const void* q, const void* k, const sol_desc* desc, float t
  *             log-sum-exp of the scaled logits over the same keys.
  */
 sol_status sol_attn_fwd(const void* q, const void* k, const void* v, const sol_desc* desc,
-                        const int16_t* blk_idx, const int32_t* blk_cnt, int32_t sink_len,
-                        float scale, void* o, float* lse, void* stream);
+                        const int16_t* blk_idx, const int32_t* blk_cnt, const int32_t* order,
+                        int32_t sink_len, float scale, void* o, float* lse, void* stream);
 
 /*
  * sol_attn_dense_fwd -- full softmax attention (routing disabled), the path

@@ -66,17 +66,17 @@ def _desc(lib, B=1, N=1000, H=2, D=128, sn=None, sh=None, sb=None):
 
 
 def _route(lib, desc, q=0x10000, k=0x20000, tau=1.0, sink=64, scale=0.0, idx=0x30000,
-           cnt=0x40000, tot=0x50000, ws=0x60000, ws_bytes=None):
+           cnt=0x40000, tot=0x50000, order=None, ws=0x60000, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = 1 << 40
     return lib.lib.sol_route(q, k, ctypes.byref(desc), ctypes.c_float(tau), sink,
-                             ctypes.c_float(scale), idx, cnt, tot, ws, ws_bytes, None)
+                             ctypes.c_float(scale), idx, cnt, tot, order, ws, ws_bytes, None)
 
 
-def _attn(lib, desc, q=0x10000, k=0x20000, v=0x30000, idx=0x40000, cnt=0x50000, sink=64,
-          scale=0.0, o=0x60000, lse=None):
-    return lib.lib.sol_attn_fwd(q, k, v, ctypes.byref(desc), idx, cnt, sink, ctypes.c_float(scale),
-                                o, lse, None)
+def _attn(lib, desc, q=0x10000, k=0x20000, v=0x30000, idx=0x40000, cnt=0x50000, order=None,
+          sink=64, scale=0.0, o=0x60000, lse=None):
+    return lib.lib.sol_attn_fwd(q, k, v, ctypes.byref(desc), idx, cnt, order, sink,
+                                ctypes.c_float(scale), o, lse, None)
 
 
 def test_workspace_size(lib):
@@ -90,14 +90,14 @@ def test_workspace_size(lib):
     ("null_desc", 1), ("D96", 2), ("N0", 1), ("negative_sink", 1), ("null_q", 1),
     ("nan_tau", 1), ("negative_tau", 1), ("nan_scale", 1), ("misaligned_q", 3),
     ("odd_stride", 3), ("small_workspace", 4), ("null_workspace", 4), ("misaligned_ws", 3),
-    ("too_many_blocks", 2), ("huge_span", 2),
+    ("misaligned_order", 3), ("too_many_blocks", 2), ("huge_span", 2),
 ])
 def test_route_argument_errors(lib, case, expect):
     d = _desc(lib)
     kw = {}
     if case == "null_desc":
         st = lib.lib.sol_route(0x10000, 0x20000, None, ctypes.c_float(1.0), 0, ctypes.c_float(0),
-                               0x30000, 0x40000, 0x50000, 0x60000, 1 << 30, None)
+                               0x30000, 0x40000, 0x50000, None, 0x60000, 1 << 30, None)
         assert st == expect
         return
     if case == "D96":
@@ -124,6 +124,8 @@ def test_route_argument_errors(lib, case, expect):
         kw["ws"] = None
     elif case == "misaligned_ws":
         kw["ws"] = 0x60010
+    elif case == "misaligned_order":
+        kw["order"] = 0x70002
     elif case == "too_many_blocks":
         d = _desc(lib, N=64 * 5000, H=1)          # 5000 candidate blocks > 4096
     elif case == "huge_span":
@@ -133,7 +135,7 @@ def test_route_argument_errors(lib, case, expect):
 
 @pytest.mark.parametrize("case,expect", [
     ("D32", 2), ("null_v", 1), ("null_idx", 1), ("misaligned_o", 3), ("misaligned_lse", 3),
-    ("negative_scale", 1), ("inf_scale", 1), ("odd_o_stride", 3),
+    ("negative_scale", 1), ("inf_scale", 1), ("odd_o_stride", 3), ("misaligned_order", 3),
 ])
 def test_attention_argument_errors(lib, case, expect):
     d = _desc(lib)
@@ -154,6 +156,8 @@ def test_attention_argument_errors(lib, case, expect):
         kw["scale"] = math.inf
     elif case == "odd_o_stride":
         d = lib.Desc(1, 1000, 2, 128, 256000, 256, 128, 256000, 260, 128)
+    elif case == "misaligned_order":
+        kw["order"] = 0x70002
     assert _attn(lib, d, **kw) == expect
 
 

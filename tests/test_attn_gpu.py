@@ -42,8 +42,8 @@ def _run(sol, w: synth.Workload, blocks=None, dense=False, tau=None):
         g = orc.geometry(w.N, w.N)
         O, L = orc.dense_attention(q32, k32, v32, blocks=blocks)
     else:
-        idx, cnt, totals = sol.route(q, k, tau, w.sink)
-        o, lse = sol.attn(q, k, v, idx, cnt, w.sink, return_lse=True)
+        idx, cnt, totals, order = sol.route(q, k, tau, w.sink)
+        o, lse = sol.attn(q, k, v, idx, cnt, w.sink, return_lse=True, order=order)
         r = orc.route(q32, k32, w.N, w.sink, tau)
         g = r.geom
         gsel = gpu_lists_to_mask(idx.cpu().numpy(), cnt.cpu().numpy(), g.NB)
@@ -141,11 +141,26 @@ def test_density_one_sparse_equals_dense_bitwise(sol):
     w = replace(synth.WORKLOADS["mid"], N=4000, H=4)
     q_bits, k_bits, v_bits = synth.make_qkv(w)
     q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
-    idx, cnt, _ = sol.route(q, k, math.inf, w.sink)
-    o1 = sol.attn(q, k, v, idx, cnt, w.sink)
+    idx, cnt, _, order = sol.route(q, k, math.inf, w.sink)
+    o1 = sol.attn(q, k, v, idx, cnt, w.sink, order=order)
     o2 = sol.attn_dense(q, k, v)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+def test_schedule_changes_no_output_bit(sol):
+    """The routing schedule (longest list first) only reorders work: outputs are
+    bit-identical with it, without it, and with a reversed schedule."""
+    import torch
+    w = replace(synth.WORKLOADS["mid"], N=5000, H=3)
+    q_bits, k_bits, v_bits = synth.make_qkv(w)
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    idx, cnt, _, order = sol.route(q, k, w.tau, w.sink)
+    outs = [sol.attn(q, k, v, idx, cnt, w.sink, order=o, return_lse=True)
+            for o in (order, None, order.flip(-1).contiguous())]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
 
 
 def test_padding_rows_contribute_exactly_zero(sol):
@@ -162,9 +177,9 @@ def test_padding_rows_contribute_exactly_zero(sol):
             t[:, : w.N] = to_dev(bits)
             bufs.append(t[:, : w.N])
         q, k, v = bufs
-        idx, cnt, tot = sol.route(q, k, w.tau, w.sink)
+        idx, cnt, tot, order = sol.route(q, k, w.tau, w.sink)
         o_full = torch.full((w.B, Np, w.H, w.D), fill, dtype=torch.bfloat16, device="cuda")
-        o = sol.attn(q, k, v, idx, cnt, w.sink, out=o_full[:, : w.N])
+        o = sol.attn(q, k, v, idx, cnt, w.sink, out=o_full[:, : w.N], order=order)
         od = sol.attn_dense(q, k, v)
         torch.cuda.synchronize()
         outs.append((o.clone(), od.clone(), cnt.clone(), tot.clone(), o_full[:, w.N:].clone()))
@@ -180,14 +195,14 @@ def test_constant_values_and_zero_queries(sol):
     w = replace(synth.WORKLOADS["mid"], N=2000, H=2)
     q_bits, k_bits, v_bits = synth.make_qkv(w)
     q, k = to_dev(q_bits), to_dev(k_bits)
-    idx, cnt, _ = sol.route(q, k, w.tau, w.sink)
+    idx, cnt, _, order = sol.route(q, k, w.tau, w.sink)
     v = torch.full_like(q, 0.375)
-    o = sol.attn(q, k, v, idx, cnt, w.sink)
+    o = sol.attn(q, k, v, idx, cnt, w.sink, order=order)
     torch.cuda.synchronize()
     assert (o.float() - 0.375).abs().max().item() <= 1e-2
     # Q = 0: the mean of the attended values (oracle closed form)
     vz = to_dev(v_bits)
-    oz = sol.attn(torch.zeros_like(q), k, vz, idx, cnt, w.sink)
+    oz = sol.attn(torch.zeros_like(q), k, vz, idx, cnt, w.sink, order=order)
     torch.cuda.synchronize()
     r = orc.route(synth.bf16_bits_to_f32(q_bits), synth.bf16_bits_to_f32(k_bits), w.N, w.sink, w.tau)
     O, _ = orc.attention(np.zeros((w.B, w.N, w.H, w.D), np.float32), synth.bf16_bits_to_f32(k_bits),
@@ -201,10 +216,10 @@ def test_strided_qkv_views_and_output(sol):
     q_bits, k_bits, v_bits = synth.make_qkv(w)
     qkv = torch.stack([to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)], dim=2)
     q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
-    idx, cnt, _ = sol.route(q, k, w.tau, w.sink)
+    idx, cnt, _, order = sol.route(q, k, w.tau, w.sink)
     obuf = torch.zeros((w.B, w.N, w.H, 2 * w.D), dtype=torch.bfloat16, device="cuda")
-    o = sol.attn(q, k, v, idx, cnt, w.sink, out=obuf[..., : w.D])
-    ref = sol.attn(to_dev(q_bits), to_dev(k_bits), to_dev(v_bits), idx, cnt, w.sink)
+    o = sol.attn(q, k, v, idx, cnt, w.sink, out=obuf[..., : w.D], order=order)
+    ref = sol.attn(to_dev(q_bits), to_dev(k_bits), to_dev(v_bits), idx, cnt, w.sink, order=order)
     torch.cuda.synchronize()
     assert torch.equal(o, ref)
     assert (obuf[..., w.D:].float() == 0).all()

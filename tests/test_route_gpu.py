@@ -30,9 +30,10 @@ def sol():
 def _route_and_check(sol, q_bits, k_bits, N, S, tau, what):
     import torch
     q, k = to_dev(q_bits), to_dev(k_bits)
-    idx, cnt, totals = sol.route(q, k, tau, S)
+    idx, cnt, totals, order = sol.route(q, k, tau, S)
     torch.cuda.synchronize()
-    idx, cnt, totals = idx.cpu().numpy(), cnt.cpu().numpy(), totals.cpu().numpy()
+    idx, cnt, totals, order = idx.cpu().numpy(), cnt.cpu().numpy(), totals.cpu().numpy(), order.cpu().numpy()
+    check_schedule(order, cnt)
     r = orc.route(synth.bf16_bits_to_f32(q_bits), synth.bf16_bits_to_f32(k_bits), N, S, tau)
     g = r.geom
     gsel = gpu_lists_to_mask(idx, cnt, g.NB)
@@ -45,6 +46,17 @@ def _route_and_check(sol, q_bits, k_bits, N, S, tau, what):
     log(f"{what}: routed {dens['route'][0]}/{dens['route'][1]} "
         f"({dens['route'][0] / max(dens['route'][1], 1):.4%}), pairs {int(totals[1])}")
     return r
+
+
+def check_schedule(order, cnt):
+    """Each row of the schedule is a permutation of the query blocks with
+    non-increasing list length (ties may come in any order)."""
+    B, H, NB = cnt.shape
+    for b in range(B):
+        for h in range(H):
+            o = order[b, h].astype(np.int64)
+            assert np.array_equal(np.sort(o), np.arange(NB)), (b, h)
+            assert np.all(np.diff(cnt[b, h][o]) <= 0), (b, h)
 
 
 @pytest.mark.parametrize("name", ["tiny", "mid"])
@@ -112,8 +124,8 @@ def test_route_strided_views_match_contiguous(sol):
     qkv = torch.stack([to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)], dim=2)   # [B, N, 3, H, D]
     q, k = qkv[:, :, 0], qkv[:, :, 1]
     assert not q.is_contiguous()
-    i1, c1, t1 = sol.route(q, k, w.tau, w.sink)
-    i2, c2, t2 = sol.route(to_dev(q_bits), to_dev(k_bits), w.tau, w.sink)
+    i1, c1, t1, _ = sol.route(q, k, w.tau, w.sink)
+    i2, c2, t2, _ = sol.route(to_dev(q_bits), to_dev(k_bits), w.tau, w.sink)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2) and torch.equal(t1, t2)
     NB = sol.num_blocks(w.N)
