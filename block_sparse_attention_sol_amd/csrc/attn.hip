@@ -200,19 +200,23 @@ attn_fwd_kernel(
         }
         v_lane = (uint32_t)r * rowstride + 16 * vchunk<D>(r, pc);
     }
-    auto issue = [&](int step, int blk) {
-        const int buf = step & 1;
-        const uint32_t row0 = (uint32_t)(64 * blk + 32 * (step & 1) + wave * T::WLOADS * T::RPL);
+    // key rows [64 blk + 32 half, +32) of K or V into the LDS half tile dst
+    auto issue_k = [&](char* dst, int blk, int half) {
+        const uint32_t row0 = (uint32_t)(64 * blk + 32 * half + wave * T::WLOADS * T::RPL);
 #pragma unroll
-        for (int m = 0; m < T::WLOADS; ++m) {
-            const uint32_t rbase = (row0 + (uint32_t)(m * T::RPL)) * rowstride;
-            const int n = wave * T::WLOADS + m;
-            load_lds16(rk, kbuf[buf] + n * 1024, k_lane[m] + rbase);
-            load_lds16(rv, vbuf[buf] + n * 1024, v_lane + rbase);
-        }
+        for (int m = 0; m < T::WLOADS; ++m)
+            load_lds16(rk, dst + (wave * T::WLOADS + m) * 1024,
+                       k_lane[m] + (row0 + (uint32_t)(m * T::RPL)) * rowstride);
+    };
+    auto issue_v = [&](char* dst, int blk, int half) {
+        const uint32_t row0 = (uint32_t)(64 * blk + 32 * half + wave * T::WLOADS * T::RPL);
+#pragma unroll
+        for (int m = 0; m < T::WLOADS; ++m)
+            load_lds16(rv, dst + (wave * T::WLOADS + m) * 1024,
+                       v_lane + (row0 + (uint32_t)(m * T::RPL)) * rowstride);
     };
 
-    // K^T-operand read offsets: lane reads row l32, logical chunk u*CHUNKS/2 + kc
+    // K operand reads: lane reads row l32, logical chunk u*CHUNKS/2 + kc
     uint32_t k_rd[T::KC];
 #pragma unroll
     for (int kc = 0; kc < T::KC; ++kc)
@@ -228,6 +232,26 @@ attn_fwd_kernel(
             v_rd[dt] = key * T::ROWB + vchunk<D>(key, byte2 >> 4) * 16 + (byte2 & 15);
         }
     }
+    auto read_k = [&](const char* src, bf16x8 (&kop)[T::KC]) {
+#pragma unroll
+        for (int kc = 0; kc < T::KC; ++kc)
+            kop[kc] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(src + k_rd[kc]));
+    };
+    auto read_v = [&](const char* src, bf16x8 (&vop)[2][T::DT]) {
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+            for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    // rows 16 c2 + 8 hf keep the row modulo 4, so the swizzle holds
+                    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)(src + v_rd[dt] + (16 * c2 + 8 * hf) * T::ROWB));
+                    const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vop[c2][dt][4 * hf + e] = xb[e];
+                }
+    };
 
     f32x16 oacc[T::DT];
 #pragma unroll
@@ -236,61 +260,35 @@ attn_fwd_kernel(
     float lsum = 0.f;         // this lane's half of the row's weight sum
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    const int nsteps = 2 * ntiles;
-    int blk = ntiles > 0 ? tile_block(0) : 0;
-    if (nsteps > 0) issue(0, blk);
-    for (int step = 0; step < nsteps; ++step) {
-        const int t = step >> 1, kt = step & 1;
-        const int buf = step & 1;
-        // this wave's loads of step `step` are done; after the barrier every
-        // wave's are, and every wave has finished reading the other buffer
-        wait_vmem_all();
-        __syncthreads();
-        bf16x8 kop[T::KC];
-#pragma unroll
-        for (int kc = 0; kc < T::KC; ++kc)
-            kop[kc] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(kbuf[buf] + k_rd[kc]));
-        bf16x8 vop[2][T::DT];
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-            for (int dt = 0; dt < T::DT; ++dt)
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    // rows 16 c2 + 8 half keep the row modulo 4, so the swizzle holds
-                    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4*)(vbuf[buf] + v_rd[dt] + (16 * c2 + 8 * half) * T::ROWB));
-                    const bf16x4 xb = __builtin_bit_cast(bf16x4, x);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) vop[c2][dt][4 * half + e] = xb[e];
-                }
-        const int cur_blk = blk;
-        if (step + 1 < nsteps) {
-            // every LDS read of this step is issued before the next step's
-            // loads, so no wait on them is needed until the next barrier
-            if (kt == 1) blk = tile_block(t + 1);
-            issue(step + 1, blk);
-        }
-
-        // S^T = K Q^T: lane holds row 32 wave + l32, keys 8 (r/4) + 4 u + r%4
+    // S^T = K Q^T for one half tile: lane holds row 32 wave + l32, keys
+    // 8 (r/4) + 4 u + r%4 of the half tile
+    auto mfma_s = [&](const bf16x8 (&kop)[T::KC]) -> f32x16 {
         f32x16 s = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < T::KC; ++kc)
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kc], qop[kc], s, 0, 0, 0);
-        const int kbase = 64 * cur_blk + 32 * kt;
-        const int kmax = tile_kmax(t, cur_blk);
-        if (kmax < kbase + 32) {
+        return s;
+    };
+    // keys >= kmax of the half tile starting at key kbase get -inf
+    auto mask = [&](f32x16& s, int kbase, int kmax) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kbase + 8 * (r / 4) + 4 * u + (r & 3);
-                if (key >= kmax) s[r] = -INFINITY;
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int key = kbase + 8 * (r / 4) + 4 * u + (r & 3);
+            if (key >= kmax) s[r] = -INFINITY;
         }
-        float mx = fmaxf(s[0], s[1]);
+    };
+    // row maximum in log2 units; lanes l and l ^ 32 hold the two halves of a row
+    auto row_max = [&](const f32x16& s) -> float {
+        float m = fmaxf(s[0], s[1]);
 #pragma unroll
-        for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
-        // every half tile holds at least one valid key, so mx is finite
+        for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(s[r], s[r + 1]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                         false, false);
+        return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+    };
+    // move the reference maximum when a row's new maximum exceeds it by more
+    // than kRescaleSlack (rare: a uniform branch off the main path)
+    auto rescale = [&](float mx) {
         if (__builtin_amdgcn_ballot_w64(mx > mref + kRescaleSlack) != 0) {
             const float mnew = fmaxf(mref, mx);
             const float f = __builtin_amdgcn_exp2f(mref - mnew);
@@ -299,10 +297,11 @@ attn_fwd_kernel(
             lsum *= f;
             mref = mnew;
         }
-        // p = exp2(s * scale_log2 - mref) rounded to bf16; l += the same
-        // rounded weights that multiply V (v_dot2 with ones, two per step)
+    };
+    // p = exp2(s * scale_log2 - mref) rounded to bf16; l += the same rounded
+    // weights that multiply V (v_dot2 with ones, two per instruction)
+    auto softmax = [&](const f32x16& s, bf16x8 (&p)[2]) {
         const float nm = -mref;
-        bf16x8 p[2];
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
             f32x8 h8;
@@ -316,12 +315,105 @@ attn_fwd_kernel(
                 lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
             }
         }
-        // O^T += V^T P^T
+    };
+    // O^T += V^T P^T
+    auto pv = [&](const bf16x8 (&vop)[2][T::DT], const bf16x8 (&p)[2]) {
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
             for (int dt = 0; dt < T::DT; ++dt)
                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c2][dt], p[c2], oacc[dt], 0, 0, 0);
+    };
+    // instruction order of one half step: LDS operand reads, the next loads,
+    // then the S MFMAs of the next half step interleaved with this half
+    // step's softmax, then the P V MFMAs interleaved with the next row maxima
+    auto schedule = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x100, T::KC + 4 * T::DT, 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 * T::WLOADS, 0);       // loads to LDS
+#pragma unroll
+        for (int i = 0; i < T::KC; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 48 / T::KC, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * T::DT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+    };
+
+    // ---- the walk, software-pipelined in 32-key half steps h = 2 t + kt.
+    // Half step h computes P V of h and S of h + 1; LDS holds K(h + 1) and
+    // V(h) when it starts, and it loads K(h + 2) and V(h + 1) into the
+    // buffers that K(h) and V(h - 1) left.  Past the end of the walk the
+    // loads repeat the last block (harmless: nothing reads the result).
+    if (ntiles > 0) {
+        int cblk = tile_block(0);
+        issue_k(kbuf[0], cblk, 0);
+        issue_v(vbuf[0], cblk, 0);
+        issue_k(kbuf[1], cblk, 1);
+        wait_vmem_all();
+        __syncthreads();
+        f32x16 s_cur;
+        {
+            bf16x8 kop[T::KC];
+            read_k(kbuf[0], kop);
+            s_cur = mfma_s(kop);
+            const int km = tile_kmax(0, cblk);
+            if (km < 64 * cblk + 32) mask(s_cur, 64 * cblk, km);
+            rescale(row_max(s_cur));
+        }
+        for (int t = 0; t < ntiles; ++t) {
+            // block of tile t + 1 (LDS list read before the wait, which any
+            // LDS read would have to take anyway)
+            const int nblk = tile_block(min(t + 1, ntiles - 1));
+            bf16x8 kop[T::KC];
+            bf16x8 vop[2][T::DT];
+            bf16x8 p[2];
+            // -- half 0 of tile t: P V(t, 0), S(t, 1)
+            wait_vmem_all();
+            __syncthreads();
+            read_k(kbuf[1], kop);            // K(t, 1)
+            read_v(vbuf[0], vop);            // V(t, 0)
+            issue_k(kbuf[0], nblk, 0);       // K(t + 1, 0)
+            issue_v(vbuf[1], cblk, 1);       // V(t, 1)
+            f32x16 s_nxt = mfma_s(kop);
+            softmax(s_cur, p);
+            pv(vop, p);
+            float mx = row_max(s_nxt);
+            schedule();
+            {
+                const int km = tile_kmax(t, cblk);
+                if (km < 64 * cblk + 64) {
+                    mask(s_nxt, 64 * cblk + 32, km);
+                    mx = row_max(s_nxt);
+                }
+            }
+            rescale(mx);
+            s_cur = s_nxt;
+            // -- half 1 of tile t: P V(t, 1), S(t + 1, 0)
+            wait_vmem_all();
+            __syncthreads();
+            read_k(kbuf[0], kop);            // K(t + 1, 0)
+            read_v(vbuf[1], vop);            // V(t, 1)
+            issue_k(kbuf[1], nblk, 1);       // K(t + 1, 1)
+            issue_v(vbuf[0], nblk, 0);       // V(t + 1, 0)
+            s_nxt = mfma_s(kop);
+            softmax(s_cur, p);
+            pv(vop, p);
+            mx = row_max(s_nxt);
+            schedule();
+            if (t + 1 < ntiles) {
+                const int km = tile_kmax(t + 1, nblk);
+                if (km < 64 * nblk + 32) {
+                    mask(s_nxt, 64 * nblk, km);
+                    mx = row_max(s_nxt);
+                }
+                rescale(mx);
+            }
+            s_cur = s_nxt;
+            cblk = nblk;
+        }
     }
 
     // ---- epilogue: normalise, round to bf16, store rows < N only
@@ -329,7 +421,9 @@ attn_fwd_kernel(
     const uint32_t obound = (uint32_t)(((int64_t)(g.N - 1) * g.osn + D) * 2);
     const __amdgpu_buffer_rsrc_t ro = rsrc(o + o_off, obound);
     const uint32_t orow = (uint32_t)(g.osn * 2);
-    const float lt = lsum + __shfl_xor(lsum, 32, 64);
+    const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
+                                                      false, false);
+    const float lt = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const uint32_t row = (uint32_t)(qb * 64 + 32 * wave + l32);
 #pragma unroll
