@@ -12,10 +12,10 @@
 //   pool_kernel          HBM-bound scan of Q and K (each element read once);
 //                        one lane owns 8 channels of one head and adds the
 //                        block's rows in ascending order.
-//   score_select_kernel  one lane owns one candidate key block and keeps its
-//                        pooled key (D floats) in registers; pooled query rows
-//                        are wave-uniform and come through the scalar cache;
-//                        each score is an FMA chain over d ascending.
+//   score_select_kernel  one lane owns one candidate key block (or a few) and
+//                        the workgroup's 16 query blocks, whose pooled rows
+//                        sit in LDS; the channels go in 8-wide chunks; each
+//                        score is an FMA chain over d ascending.
 #include "sol_internal.h"
 
 namespace sol {
@@ -99,7 +99,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
 }
 
-constexpr int kMaxWaves = 8;
+constexpr int kMaxWaves = 16;
 
 // grid: x = query-block tiles of TI (XCD-remapped together with y), y = B * H
 // block: 64 * W threads; lane slot s = jj * 64 W + tid owns candidate j = j0 + s.
@@ -125,32 +125,60 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
     const float* qb = qbar + (int64_t)bh * g.NB * D;
     const float* kb = kbar + (int64_t)bh * (D / 8) * g.NB * 8;
 
-    float sc[JPL][TI];
+    // scores: each lane owns JPL candidates and the TI query blocks of the
+    // workgroup.  The TI pooled query rows are staged in LDS once and read
+    // back as broadcasts; the channels go in 8-wide chunks, so a lane loads
+    // 32 bytes of k-bar per chunk and each q-bar value feeds JPL FMAs.  Every
+    // score is still one FMA chain over d ascending.
+    __shared__ __attribute__((aligned(16))) float qs[TI][D];
+    // the workgroup's totals, added to the global ones with one atomic each
+    __shared__ unsigned long long wg_tot[2];
+    if (tid == 0) {
+        wg_tot[0] = 0;
+        wg_tot[1] = 0;
+    }
+    for (int e = tid; e < TI * D; e += blockDim.x) {
+        const int ii = e / D;
+        qs[ii][e - ii * D] = ii < ni ? qb[(int64_t)(i0 + ii) * D + (e - ii * D)] : 0.f;
+    }
+    __syncthreads();
+    int jrow[JPL];
+    bool jvalid[JPL];
+    float acc[JPL][TI];
 #pragma unroll
     for (int jj = 0; jj < JPL; ++jj) {
         const int s = jj * slots + tid;
-        const bool valid = s < g.ncand;
-        const int j = g.j0 + (valid ? s : 0);
-        float kv[D];
+        jvalid[jj] = s < g.ncand;
+        jrow[jj] = g.j0 + (jvalid[jj] ? s : 0);
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-            const float4* p = (const float4*)(kb + ((int64_t)c * g.NB + j) * 8);
+        for (int ii = 0; ii < TI; ++ii) acc[jj][ii] = 0.f;
+    }
+    for (int c = 0; c < D / 8; ++c) {
+        float kv[JPL][8];
+#pragma unroll
+        for (int jj = 0; jj < JPL; ++jj) {
+            const float4* p = (const float4*)(kb + ((int64_t)c * g.NB + jrow[jj]) * 8);
             const float4 a = p[0], b = p[1];
-            kv[8 * c + 0] = a.x; kv[8 * c + 1] = a.y; kv[8 * c + 2] = a.z; kv[8 * c + 3] = a.w;
-            kv[8 * c + 4] = b.x; kv[8 * c + 5] = b.y; kv[8 * c + 6] = b.z; kv[8 * c + 7] = b.w;
+            kv[jj][0] = a.x; kv[jj][1] = a.y; kv[jj][2] = a.z; kv[jj][3] = a.w;
+            kv[jj][4] = b.x; kv[jj][5] = b.y; kv[jj][6] = b.z; kv[jj][7] = b.w;
         }
 #pragma unroll
         for (int ii = 0; ii < TI; ++ii) {
-            float acc = 0.f;
-            if (ii < ni) {
-                const float* qr = qb + (int64_t)(i0 + ii) * D;
+            const float4 qa = *(const float4*)&qs[ii][8 * c];
+            const float4 qc = *(const float4*)&qs[ii][8 * c + 4];
+            const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qc.x, qc.y, qc.z, qc.w};
 #pragma unroll
-                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qr[d], kv[d], acc);
-            }
-            const float v = acc * scale;
-            sc[jj][ii] = valid ? v : -INFINITY;
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int jj = 0; jj < JPL; ++jj)
+                    acc[jj][ii] = __builtin_fmaf(qv[e], kv[jj][e], acc[jj][ii]);
         }
     }
+    float sc[JPL][TI];
+#pragma unroll
+    for (int jj = 0; jj < JPL; ++jj)
+#pragma unroll
+        for (int ii = 0; ii < TI; ++ii) sc[jj][ii] = jvalid[jj] ? acc[jj][ii] * scale : -INFINITY;
 
     // row maxima over all candidates of the workgroup
 #pragma unroll
@@ -199,8 +227,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
         }
         cnt[(int64_t)bh * g.NB + i0 + tid] = run;
         const int rows = min(kBlock, g.N - kBlock * (i0 + tid));
-        atomicAdd((unsigned long long*)&totals[0], (unsigned long long)run);
-        atomicAdd((unsigned long long*)&totals[1], (unsigned long long)rows * g.Ssink);
+        atomicAdd(&wg_tot[0], (unsigned long long)run);
+        atomicAdd(&wg_tot[1], (unsigned long long)rows * g.Ssink);
     }
     __syncthreads();
 #pragma unroll
@@ -217,8 +245,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
         }
     }
     keys_local = wave_sum(keys_local);
-    if (lane == 0 && keys_local != 0)
-        atomicAdd((unsigned long long*)&totals[1], (unsigned long long)keys_local);
+    if (lane == 0 && keys_local != 0) atomicAdd(&wg_tot[1], (unsigned long long)keys_local);
+    __syncthreads();
+    if (tid == 0) {
+        atomicAdd((unsigned long long*)&totals[0], wg_tot[0]);
+        atomicAdd((unsigned long long*)&totals[1], wg_tot[1]);
+    }
 }
 
 // S >= N: no candidates, every list is empty, only sink pairs are attended;
@@ -291,7 +323,9 @@ hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, fl
                          float tau, int16_t* idx, int32_t* cnt, int64_t* totals,
                          hipStream_t stream)
 {
-    const int jpl = (g.ncand + 64 * kMaxWaves - 1) / (64 * kMaxWaves);
+    // candidates per lane: up to 4, so each q-bar value read from LDS feeds
+    // up to 4 FMAs; 16 waves x 64 lanes x 4 cover the 4096-candidate limit
+    const int jpl = g.ncand <= 64 ? 1 : g.ncand <= 128 ? 2 : 4;
     const int W = (g.ncand + 64 * jpl - 1) / (64 * jpl);
 #define SOL_SELECT_CASE(J, T)                                                               \
     do {                                                                                    \
@@ -301,10 +335,9 @@ hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, fl
         hipLaunchKernelGGL((score_select_kernel<D, J, T>), dim3(grid), dim3(64 * W), 0,     \
                            stream, qbar, kbar, g, scale, tau, tiles, idx, cnt, totals);     \
     } while (0)
-    if (jpl <= 1) SOL_SELECT_CASE(1, 16);
-    else if (jpl <= 2) SOL_SELECT_CASE(2, 16);
-    else if (jpl <= 4) SOL_SELECT_CASE(4, 8);
-    else SOL_SELECT_CASE(8, 4);
+    if (jpl == 1) SOL_SELECT_CASE(1, 16);
+    else if (jpl == 2) SOL_SELECT_CASE(2, 16);
+    else SOL_SELECT_CASE(4, 16);
 #undef SOL_SELECT_CASE
     return hipGetLastError();
 }
