@@ -82,16 +82,41 @@ __global__ __launch_bounds__(256) void pool_kernel(
     }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
+// reductions over the 64 lanes of a wave, result in every lane: DPP within
+// rows of 16 lanes, then a swizzle across 16 and a permlane swap across 32
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float swz16(float v) {       // lane ^ 16 within each 32
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+__device__ __forceinline__ uint32_t swz16(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
 }
 
-__device__ __forceinline__ long long wave_sum(long long v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));      // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp<0x4E>(v));      // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp<0x141>(v));     // row_half_mirror
+    v = fmaxf(v, dpp<0x140>(v));     // row_mirror
+    v = fmaxf(v, swz16(v));
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    v += dpp<0x140>(v);
+    v += swz16(v);
+    const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return sw[0] + sw[1];
 }
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
@@ -198,32 +223,33 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
         thr[ii] = m - tau;
     }
 
-    // selection: count per (query block, slot group, wave)
-    long long keys_local = 0;
+    // selection.  Pass 1: each wave's ballot per (query block, candidate
+    // slot) goes to LDS, and each lane sums the attended (row, key) pairs of
+    // its selected candidates.
+    __shared__ unsigned long long balls[TI][JPL * kMaxWaves];
+    uint32_t keys_local = 0;
 #pragma unroll
     for (int ii = 0; ii < TI; ++ii) {
         const int i = i0 + ii;
+        const uint32_t rows = (uint32_t)max(min(kBlock, g.N - kBlock * i), 0);
 #pragma unroll
         for (int jj = 0; jj < JPL; ++jj) {
-            const int s = jj * slots + tid;
-            const int j = g.j0 + s;
-            const bool sel = (ii < ni) && (s < g.ncand) && (sc[jj][ii] >= thr[ii] || j == i);
+            const int sl = jj * slots + tid;
+            const int j = g.j0 + sl;
+            const bool sel = (ii < ni) && jvalid[jj] && (sc[jj][ii] >= thr[ii] || j == i);
             const uint64_t bal = __ballot(sel);
-            if (lane == 0) wcount[ii][jj * W + wave] = __popcll(bal);
-            if (sel) {
-                const int rows = min(kBlock, g.N - kBlock * i);
-                const int keys = min(kBlock * j + kBlock, g.N) - max(kBlock * j, g.S);
-                keys_local += (long long)rows * keys;
-            }
+            if (lane == 0) balls[ii][jj * W + wave] = bal;
+            const uint32_t keys = (uint32_t)(min(kBlock * j + kBlock, g.N) - max(kBlock * j, g.S));
+            keys_local += sel ? rows * keys : 0u;
         }
     }
     __syncthreads();
+    // counts and list offsets: one thread per query block
     if (tid < ni) {
         int run = 0;
         for (int e = 0; e < JPL * W; ++e) {
-            const int jj = e / W, w = e - jj * W;
-            woffset[tid][jj * W + w] = run;
-            run += wcount[tid][jj * W + w];
+            woffset[tid][e] = run;
+            run += __popcll(balls[tid][e]);
         }
         cnt[(int64_t)bh * g.NB + i0 + tid] = run;
         const int rows = min(kBlock, g.N - kBlock * (i0 + tid));
@@ -231,21 +257,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
         atomicAdd(&wg_tot[1], (unsigned long long)rows * g.Ssink);
     }
     __syncthreads();
+    // pass 2: compaction into ascending lists (slot order = block order)
 #pragma unroll
     for (int ii = 0; ii < TI; ++ii) {
-        const int i = i0 + ii;
-        int16_t* row = idx + ((int64_t)bh * g.NB + (ii < ni ? i : 0)) * g.NB;
+        if (ii >= ni) break;
+        int16_t* row = idx + ((int64_t)bh * g.NB + i0 + ii) * g.NB;
 #pragma unroll
         for (int jj = 0; jj < JPL; ++jj) {
-            const int s = jj * slots + tid;
-            const int j = g.j0 + s;
-            const bool sel = (ii < ni) && (s < g.ncand) && (sc[jj][ii] >= thr[ii] || j == i);
-            const uint64_t bal = __ballot(sel);
-            if (sel) row[woffset[ii][jj * W + wave] + lanes_below(bal)] = (int16_t)j;
+            const uint64_t bal = balls[ii][jj * W + wave];
+            if ((bal >> lane) & 1)
+                row[woffset[ii][jj * W + wave] + lanes_below(bal)] = (int16_t)(g.j0 + jj * slots + tid);
         }
     }
-    keys_local = wave_sum(keys_local);
-    if (lane == 0 && keys_local != 0) atomicAdd(&wg_tot[1], (unsigned long long)keys_local);
+    const uint32_t wsum = wave_sum(keys_local);
+    if (lane == 0 && wsum != 0) atomicAdd(&wg_tot[1], (unsigned long long)wsum);
     __syncthreads();
     if (tid == 0) {
         atomicAdd((unsigned long long*)&totals[0], wg_tot[0]);
@@ -337,7 +362,7 @@ hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, fl
     } while (0)
     if (jpl == 1) SOL_SELECT_CASE(1, 16);
     else if (jpl == 2) SOL_SELECT_CASE(2, 16);
-    else SOL_SELECT_CASE(4, 16);
+    else SOL_SELECT_CASE(4, 8);
 #undef SOL_SELECT_CASE
     return hipGetLastError();
 }
