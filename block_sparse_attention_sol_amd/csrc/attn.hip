@@ -324,11 +324,15 @@ attn_fwd_kernel(
             for (int dt = 0; dt < T::DT; ++dt)
                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c2][dt], p[c2], oacc[dt], 0, 0, 0);
     };
+    // LDS reads complete in issue order (lgkmcnt), so the K operand reads go
+    // out first and alone: queued behind the slower transposed V reads they
+    // would hold back the S MFMAs of the whole half step
+    auto k_first = [&]() { __builtin_amdgcn_sched_barrier(0); };
     // instruction order of one half step: LDS operand reads, the next loads,
     // then the S MFMAs of the next half step interleaved with this half
     // step's softmax, then the P V MFMAs interleaved with the next row maxima
     auto schedule = [&]() {
-        __builtin_amdgcn_sched_group_barrier(0x100, T::KC + 4 * T::DT, 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * T::DT, 0);           // V^T LDS reads
         __builtin_amdgcn_sched_group_barrier(0x020, 2 * T::WLOADS, 0);       // loads to LDS
 #pragma unroll
         for (int i = 0; i < T::KC; ++i) {
@@ -374,6 +378,7 @@ attn_fwd_kernel(
             wait_vmem_all();
             __syncthreads();
             read_k(kbuf[1], kop);            // K(t, 1)
+            k_first();
             read_v(vbuf[0], vop);            // V(t, 0)
             issue_k(kbuf[0], nblk, 0);       // K(t + 1, 0)
             issue_v(vbuf[1], cblk, 1);       // V(t, 1)
@@ -395,6 +400,7 @@ attn_fwd_kernel(
             wait_vmem_all();
             __syncthreads();
             read_k(kbuf[0], kop);            // K(t + 1, 0)
+            k_first();
             read_v(vbuf[1], vop);            // V(t, 1)
             issue_k(kbuf[1], nblk, 1);       // K(t + 1, 1)
             issue_v(vbuf[0], nblk, 0);       // V(t + 1, 0)
