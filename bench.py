@@ -38,7 +38,7 @@ def src_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(launch_bytes: float):
+def measured_traffic():
     """HBM bytes per attention launch from the committed rocprofv3 counter runs,
     or None when the kernel source changed since they were taken."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -47,6 +47,46 @@ def measured_traffic(launch_bytes: float):
     if t.get("attn_src_sha256_16") != src_hash(ATTN_SRC):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def _counter_kib(csv_path: str, kernel_substr: str, counter: str) -> list:
+    """Per-dispatch values (KiB) of one counter for kernels whose name contains kernel_substr."""
+    import csv
+    vals = []
+    for r in csv.DictReader(open(csv_path)):
+        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def record_traffic(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str,
+                   copy_bytes: int) -> dict:
+    """HBM traffic of one sparse attention launch at the pages' shape from rocprofv3
+    counter collections: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the attention
+    kernel, each scaled by what the same counter reads for a plain device copy of
+    copy_bytes bytes (the copy reads and writes copy_bytes each)."""
+    import numpy as np
+    fetch = np.mean(_counter_kib(fetch_csv, "attn_fwd_kernel<128, false>", "FETCH_SIZE"))
+    write = np.mean(_counter_kib(write_csv, "attn_fwd_kernel<128, false>", "WRITE_SIZE"))
+    cf = np.mean(_counter_kib(copy_fetch_csv, "copyBuffer", "FETCH_SIZE"))
+    cw = np.mean(_counter_kib(copy_write_csv, "copyBuffer", "WRITE_SIZE"))
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    rec = {
+        "attn_src_sha256_16": src_hash(ATTN_SRC),
+        "fetch_kib_per_launch": round(float(fetch), 1),
+        "write_kib_per_launch": round(float(write), 1),
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": round(float(cf), 1),
+        "copy_write_kib": round(float(cw), 1),
+        "fetch_scale": round(float(f_scale), 4),
+        "write_scale": round(float(w_scale), 4),
+        "hbm_bytes_per_launch": int(fetch * 1024.0 * f_scale + write * 1024.0 * w_scale),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
 
 
 def cpu_baseline(w, q_bits, k_bits, v_bits, n_heads: int, n_blocks: int, flop_eff: float):
@@ -105,7 +145,17 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (for scaling "
                          "the HBM counters FETCH_SIZE / WRITE_SIZE) and exit")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                         "COPY_WRITE_CSV"),
+                    help="write the attention kernel's HBM bytes per launch from rocprofv3 "
+                         "counter CSVs (no GPU needed) and exit")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30,
+                    help="size of the copy behind COPY_*_CSV (default 1 GiB)")
     args = ap.parse_args()
+    if args.record_traffic:
+        rec = record_traffic(*args.record_traffic, copy_bytes=args.copy_bytes)
+        print(json.dumps(rec))
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         err(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
@@ -206,7 +256,7 @@ def main() -> int:
         f"{(route_gbs or 0):.0f} GB/s; route density {rho_route:.4%}, pair density {rho_pair:.4%}; "
         f"wall {wall:.2f} s for {args.steps} steps")
 
-    traffic = measured_traffic(flop_eff)
+    traffic = measured_traffic()
     rec = {
         "metric": "ms/forward + effective TFLOP/s (MFMA % peak) at [1,38247,56,128], ~19% density",
         "value": round(tflops, 2),
