@@ -10,7 +10,8 @@
 // then the routed tiles gives exactly the log-sum-exp merge of the two parts.
 //
 // Work decomposition: one workgroup of two waves per (batch, head, query
-// block); wave w owns query rows 32 w .. 32 w + 31 of the block.  The walk
+// block); wave w owns query rows 32 w .. 32 w + 31 of the block (the dense
+// walk, the same for every block, takes two blocks and four waves).  The walk
 // goes in 32-key half steps.  Both waves fetch the K and V half tile of the
 // next step straight from global memory into LDS (buffer loads with the LDS
 // destination, 16 bytes per lane) while they compute the current one, so the
@@ -77,7 +78,7 @@ __device__ __forceinline__ void wait_vmem_all() {
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
-template <int D>
+template <int D, int NW = 2>
 struct Tile {
     static constexpr int KC = D / 16;             // MFMA k-steps over the head dimension
     static constexpr int DT = D / 32;             // 32-wide output channel tiles
@@ -85,7 +86,7 @@ struct Tile {
     static constexpr int CHUNKS = ROWB / 16;      // 16-byte chunks per key row
     static constexpr int HB = 32 * ROWB;          // bytes of a 32-key half tile (K or V)
     static constexpr int LOADS = HB / 1024;       // 1 KB wave loads per half tile
-    static constexpr int WLOADS = LOADS / 2;      // ... issued by each of the two waves
+    static constexpr int WLOADS = LOADS / NW;     // ... issued by each of the NW waves
     static constexpr int RPL = 1024 / ROWB;       // key rows per 1 KB load
 };
 
@@ -107,32 +108,43 @@ __device__ __forceinline__ int vchunk(int key, int c) {
 constexpr int kMaxList = 4096;   // routed blocks per query block (candidate limit)
 
 template <int D, bool DENSE>
-__global__ __launch_bounds__(128) void
+__global__ __launch_bounds__(DENSE ? 256 : 128) void
 attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, Geom g, const int16_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ order, float scale_log2,
     uint16_t* __restrict__ o, float* __restrict__ lse)
 {
-    using T = Tile<D>;
+    // query blocks per workgroup: the dense walk is the same for every query
+    // block, so two blocks (128 rows, four waves) share each fetched tile;
+    // routed walks differ per block, so they get one block (two waves) each
+    constexpr int NQ = DENSE ? 2 : 1;
+    constexpr int NW = 2 * NQ;
+    using T = Tile<D, NW>;
     __shared__ __attribute__((aligned(1024))) char kbuf[2][T::HB];
     __shared__ __attribute__((aligned(1024))) char vbuf[2][T::HB];
     // routed list of this query block: round_up(min(ncand, kMaxList), 128)
     // entries of dynamic LDS, sized at launch
     extern __shared__ __attribute__((aligned(16))) int16_t lst[];
 
-    const int work = xcd_remap(blockIdx.x, gridDim.x, g.B * g.H * g.NB);
+    const int nbw = (g.NB + NQ - 1) / NQ;                  // workgroups per (batch, head)
+    const int work = xcd_remap(blockIdx.x, gridDim.x, g.B * g.H * nbw);
     if (work < 0) return;
-    const int bh = work / g.NB;
+    const int bh = work / nbw;
     // the rank-th query block of this (batch, head) in the routing schedule
     // (longest list first), or in sequence order without one
-    const int rank = work - bh * g.NB;
-    const int qb = (DENSE || order == nullptr)
-                       ? rank : min(max(order[(int64_t)bh * g.NB + rank], 0), g.NB - 1);
+    const int rank = work - bh * nbw;
+    const int qb = DENSE ? NQ * rank
+                 : order == nullptr ? rank
+                                    : min(max(order[(int64_t)bh * g.NB + rank], 0), g.NB - 1);
     const int item = bh * g.NB + qb;
     const int b = bh / g.H, h = bh - b * g.H;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // wave w owns rows 32 (w & 1) .. +31 of query block qb + (w >> 1); past the
+    // last block (odd NB, dense) it repeats the last block, whose rows it then
+    // writes with the same values as its partner waves
+    const int qrow0 = min(qb + (wave >> 1), g.NB - 1) * 64 + 32 * (wave & 1);
     const int lane = tid & 63;
     const int l32 = lane & 31, u = lane >> 5;
 
@@ -146,7 +158,7 @@ attn_fwd_kernel(
     // ---- Q^T operand of this wave's 32 rows, resident for the whole walk
     bf16x8 qop[T::KC];
     {
-        const uint32_t base = (uint32_t)(qb * 64 + 32 * wave + l32) * rowstride + u * D;
+        const uint32_t base = (uint32_t)(qrow0 + l32) * rowstride + u * D;
 #pragma unroll
         for (int kc = 0; kc < T::KC; ++kc) qop[kc] = load16(rq, base + 16 * kc);
     }
@@ -160,7 +172,7 @@ attn_fwd_kernel(
             // 2-byte loads: buffer range checks work per dword, so a wider load
             // would drop the last entry of an odd-length list
             const __amdgpu_buffer_rsrc_t rl = rsrc(idx + (int64_t)item * g.NB, (uint32_t)nlist * 2);
-            for (int base = 0; base < nlist; base += 128)
+            for (int base = 0; base < nlist; base += 64 * NW)
                 lst[base + tid] = (int16_t)__builtin_amdgcn_raw_buffer_load_b16(
                     rl, (uint32_t)(2 * (base + tid)), 0, 0);
         }
@@ -187,9 +199,8 @@ attn_fwd_kernel(
     // ---- global -> LDS half-tile loads.  Wave load n (this wave issues
     // n = wave * WLOADS + m) fills LDS bytes [n * 1024, +1024): lane l writes
     // half-tile row n * RPL + l / CHUNKS at physical chunk l % CHUNKS, so it
-    // fetches the logical chunk that the swizzle puts there.  The swizzle only
-    // depends on m and the lane (n * RPL differs between the waves by a
-    // multiple of CHUNKS), so the lane offsets are precomputed per m.
+    // fetches the logical chunk that the swizzle puts there.  The lane offsets
+    // depend only on the wave, m and the lane, so they are precomputed per m.
     uint32_t k_lane[T::WLOADS], v_lane;
     {
         const int r = lane / T::CHUNKS, pc = lane % T::CHUNKS;
@@ -431,7 +442,7 @@ attn_fwd_kernel(
                                                       false, false);
     const float lt = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const uint32_t row = (uint32_t)(qb * 64 + 32 * wave + l32);
+    const uint32_t row = (uint32_t)(qrow0 + l32);
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
@@ -456,11 +467,12 @@ hipError_t launch(const Geom& g, const void* q, const void* k, const void* v,
                   const int16_t* idx, const int32_t* cnt, const int32_t* order, float scale,
                   void* o, float* lse, hipStream_t stream)
 {
-    const int total = g.B * g.H * g.NB;
+    constexpr int NQ = DENSE ? 2 : 1;
+    const int total = g.B * g.H * ((g.NB + NQ - 1) / NQ);
     const int grid = round_up(total, kXcds);
     const float scale_log2 = scale * 1.4426950408889634f;
     const size_t lds_list = DENSE ? 0 : (size_t)round_up(min(g.ncand, kMaxList), 128) * sizeof(int16_t);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE>), dim3(grid), dim3(128), lds_list, stream,
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DENSE>), dim3(grid), dim3(64 * 2 * NQ), lds_list, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, g, idx, cnt,
                        order, scale_log2, (uint16_t*)o, lse);
     return hipGetLastError();
