@@ -129,6 +129,26 @@ sol_status sol_attn_dense_fwd(const void* q, const void* k, const void* v, const
     return attn_common(q, k, v, desc, nullptr, nullptr, nullptr, 0, scale, o, lse, true, stream);
 }
 
+sol_status sol_gate_fwd(const void* q, const void* k, const void* v, const sol_desc* desc,
+                        const int16_t* blk_idx, const int32_t* blk_cnt, const int32_t* order,
+                        int32_t sink_len, float scale, void* o_sparse, void* o_dense,
+                        double* stats, void* stream) {
+    if (stats == nullptr || o_dense == nullptr) return SOL_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(stats) & 7u) != 0 || !aligned16(o_dense)) return SOL_ERR_ALIGN;
+    if (o_dense == o_sparse) return SOL_ERR_ARG;
+    sol_status st = attn_common(q, k, v, desc, blk_idx, blk_cnt, order, sink_len, scale, o_sparse,
+                                nullptr, false, stream);
+    if (st != SOL_OK) return st;
+    st = attn_common(q, k, v, desc, nullptr, nullptr, nullptr, 0, scale, o_dense, nullptr, true,
+                     stream);
+    if (st != SOL_OK) return st;
+    sol::Geom g;
+    check_desc(desc, sink_len, &g);
+    const hipError_t e = sol::launch_gate(g, o_sparse, o_dense, stats,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOL_OK : SOL_ERR_HIP;
+}
+
 const char* sol_status_str(sol_status status) {
     switch (status) {
         case SOL_OK: return "ok";

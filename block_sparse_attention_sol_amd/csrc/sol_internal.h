@@ -45,4 +45,8 @@ hipError_t launch_attn(const Geom& g, const void* q, const void* k, const void* 
                        const int16_t* idx, const int32_t* cnt, const int32_t* order, float scale,
                        void* o, float* lse, bool dense, hipStream_t stream);
 
+// Sparse-vs-dense gate statistics (float64[5]) of two outputs with O strides.
+hipError_t launch_gate(const Geom& g, const void* a, const void* b, double* stats,
+                       hipStream_t stream);
+
 }  // namespace sol

@@ -49,6 +49,8 @@ def _load():
     lib.sol_attn_fwd.restype = ctypes.c_int
     lib.sol_attn_dense_fwd.argtypes = [vp, vp, vp, dp, f32, vp, vp, vp]
     lib.sol_attn_dense_fwd.restype = ctypes.c_int
+    lib.sol_gate_fwd.argtypes = [vp, vp, vp, dp, vp, vp, vp, i32, f32, vp, vp, vp, vp]
+    lib.sol_gate_fwd.restype = ctypes.c_int
     lib.sol_status_str.argtypes, lib.sol_status_str.restype = [ctypes.c_int], ctypes.c_char_p
     _ = i64
     return lib
@@ -159,6 +161,28 @@ def attn_dense(q, k, v, scale: float = 0.0, out=None, return_lse=False):
                                 lse.data_ptr() if lse is not None else None, _stream(q))
     _check(st, "sol_attn_dense_fwd")
     return (o, lse) if return_lse else o
+
+
+def gate(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, order=None):
+    """Sparse-vs-dense gate: returns (o_sparse, o_dense, stats) with stats a float64
+    tensor [max_abs, sum_abs, sum_sq_diff, sum_sq_dense, count] on q's device."""
+    _check_qkv(q, k, v)
+    o_s, o_d = torch.empty_like(q), torch.empty_like(q)
+    stats = torch.empty(5, dtype=torch.float64, device=q.device)
+    st = lib.sol_gate_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(make_desc(q, o_s)),
+                          blk_idx.data_ptr(), blk_cnt.data_ptr(),
+                          order.data_ptr() if order is not None else None, int(sink),
+                          ctypes.c_float(scale), o_s.data_ptr(), o_d.data_ptr(), stats.data_ptr(),
+                          _stream(q))
+    _check(st, "sol_gate_fwd")
+    return o_s, o_d, stats
+
+
+def gate_summary(stats) -> dict:
+    """max-abs, mean-abs and relative-L2 error from sol_gate_fwd's statistics."""
+    s = stats.cpu().tolist()
+    return {"max_abs": s[0], "mean_abs": s[1] / max(s[4], 1.0),
+            "l2_rel": math.sqrt(s[2] / s[3]) if s[3] > 0 else 0.0}
 
 
 def forward(q, k, v, tau: float, sink: int, scale: float = 0.0, return_lse=False):

@@ -153,6 +153,29 @@ sol_status sol_attn_fwd(const void* q, const void* k, const void* v, const sol_d
 sol_status sol_attn_dense_fwd(const void* q, const void* k, const void* v, const sol_desc* desc,
                               float scale, void* o, float* lse, void* stream);
 
+/*
+ * sol_gate_fwd -- the sparse-vs-dense correctness gate: one sparse forward
+ * (as sol_attn_fwd) into o_sparse and one dense forward (as
+ * sol_attn_dense_fwd) into o_dense of the same inputs, then their error
+ * statistics over the valid rows (tokenfactory.fast post, "Verification
+ * that catches what the metrics miss": the gate compares the two outputs
+ * inside one attention call; clawpit.io article, paragraph on the Sol-Attn
+ * settings: reported as maximum, mean and relative L2 error).
+ *
+ *   o_sparse, o_dense  out, [B, N, H, D] bf16 with the O strides of desc;
+ *                      distinct buffers.
+ *   stats     out, device float64 [5], 8-byte aligned: [0] max |s - d|,
+ *             [1] sum |s - d|, [2] sum (s - d)^2, [3] sum d^2, [4] number
+ *             of elements compared.  Mean = [1] / [4]; relative L2 =
+ *             sqrt([2] / [3]).  The maximum is exact; the sums are float64
+ *             atomics whose last bits depend on completion order.
+ * Other arguments and errors as for sol_attn_fwd.
+ */
+sol_status sol_gate_fwd(const void* q, const void* k, const void* v, const sol_desc* desc,
+                        const int16_t* blk_idx, const int32_t* blk_cnt, const int32_t* order,
+                        int32_t sink_len, float scale, void* o_sparse, void* o_dense,
+                        double* stats, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* sol_status_str(sol_status status);
 

@@ -170,3 +170,22 @@ def test_dense_argument_errors(lib):
     st = lib.lib.sol_attn_dense_fwd(0x10000, None, 0x30000, ctypes.byref(d), ctypes.c_float(0),
                                     0x40000, None, None)
     assert st == 1
+
+
+def test_gate_argument_errors(lib):
+    d = _desc(lib)
+    stats = 0x80000
+
+    def gate(**kw):
+        a = dict(q=0x10000, k=0x20000, v=0x30000, idx=0x40000, cnt=0x50000, order=None, sink=64,
+                 scale=0.0, os=0x60000, od=0x70000, stats=stats)
+        a.update(kw)
+        return lib.lib.sol_gate_fwd(a["q"], a["k"], a["v"], ctypes.byref(d), a["idx"], a["cnt"],
+                                    a["order"], a["sink"], ctypes.c_float(a["scale"]), a["os"],
+                                    a["od"], a["stats"], None)
+    assert gate(stats=None) == 1
+    assert gate(od=None) == 1
+    assert gate(od=0x60000) == 1            # the two outputs must differ
+    assert gate(stats=0x80004) == 3         # float64 statistics need 8-byte alignment
+    assert gate(od=0x70002) == 3
+    assert gate(sink=-1) == 1

@@ -264,3 +264,37 @@ def test_varlen_sixteen_lengths_one_build_stable_time(sol):
     assert worst <= 1.15
     # the very first call (code objects already loaded at import) is no outlier
     assert first_ms <= 20 * float(np.median(best_ms))
+
+
+@pytest.mark.parametrize("name,N,H", [("tiny", 1024, 4), ("mid", 3001, 3)])
+def test_sparse_vs_dense_gate(sol, name, N, H):
+    """sol_gate_fwd: its statistics equal numpy's on the two outputs it returns,
+    both outputs match the oracle, and the gate's error matches the oracle's
+    sparse-vs-dense error (float64 on both sides)."""
+    import torch
+    w = replace(synth.WORKLOADS[name], N=N, H=H)
+    q_bits, k_bits, v_bits = synth.make_qkv(w)
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    idx, cnt, _, order = sol.route(q, k, w.tau, w.sink)
+    o_s, o_d, stats = sol.gate(q, k, v, idx, cnt, w.sink, order=order)
+    torch.cuda.synchronize()
+    a, b = bf16_tensor_to_f64(o_s), bf16_tensor_to_f64(o_d)
+    st = stats.cpu().numpy()
+    diff = a - b
+    assert st[0] == np.abs(diff).max()
+    assert st[4] == diff.size
+    np.testing.assert_allclose(st[1], np.abs(diff).sum(), rtol=1e-9)
+    np.testing.assert_allclose(st[2], (diff ** 2).sum(), rtol=1e-9)
+    np.testing.assert_allclose(st[3], (b ** 2).sum(), rtol=1e-9)
+    q32, k32, v32 = (synth.bf16_bits_to_f32(x) for x in (q_bits, k_bits, v_bits))
+    r = orc.route(q32, k32, w.N, w.sink, w.tau)
+    Os, _ = orc.attention(q32, k32, v32, r.sel, r.geom)
+    Od, _ = orc.dense_attention(q32, k32, v32)
+    assert_close(a, Os, f"gate {name} sparse")
+    assert_close(b, Od, f"gate {name} dense")
+    summ = sol.gate_summary(stats)
+    ref_l2 = float(np.linalg.norm(Os - Od) / np.linalg.norm(Od))
+    ref_mean = float(np.abs(Os - Od).mean())
+    log(f"gate {name}: {summ}; oracle l2_rel {ref_l2:.5f} mean_abs {ref_mean:.5f}")
+    assert abs(summ["l2_rel"] - ref_l2) <= 5e-3 + 0.02 * ref_l2
+    assert abs(summ["mean_abs"] - ref_mean) <= 2e-3 + 0.02 * ref_mean
