@@ -33,6 +33,12 @@ sol_status check_desc(const sol_desc* d, int32_t sink_len, sol::Geom* g) {
     const int64_t span_out = ((64 * NB - 1) * d->o_sn + d->D) * 2;
     if (span_in >= ((int64_t)1 << 32) || span_out >= ((int64_t)1 << 32)) return SOL_ERR_UNSUPPORTED;
     if ((int64_t)d->H * d->N >= ((int64_t)1 << 30)) return SOL_ERR_UNSUPPORTED;
+    if (d->cu_seqlens != nullptr) {
+        // packed variable-length batch: rows are addressed through the offsets
+        if (d->qkv_sb != 0 || d->o_sb != 0 || d->total_rows < 0) return SOL_ERR_ARG;
+        if (d->total_rows > INT32_MAX) return SOL_ERR_UNSUPPORTED;
+        if ((reinterpret_cast<uintptr_t>(d->cu_seqlens) & 3u) != 0) return SOL_ERR_ALIGN;
+    }
 
     g->B = d->B;
     g->N = d->N;
@@ -49,6 +55,8 @@ sol_status check_desc(const sol_desc* d, int32_t sink_len, sol::Geom* g) {
     g->osb = d->o_sb;
     g->osn = d->o_sn;
     g->osh = d->o_sh;
+    g->cu = d->cu_seqlens;
+    g->T = d->cu_seqlens != nullptr ? d->total_rows : 0;
     return SOL_OK;
 }
 

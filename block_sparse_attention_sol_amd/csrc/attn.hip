@@ -31,7 +31,10 @@
 // Every global access goes through a buffer descriptor bounded at the last
 // valid row of its (batch, head), with the whole offset in the VGPR operand:
 // rows >= N read as zero and are never written, so any N runs on the one
-// build and padding contributes exactly 0.
+// build and padding contributes exactly 0.  In a packed variable-length batch
+// each sample brings its own row offset and length N; the grid is sized by
+// the longest sample, and workgroups past a shorter sample's last block exit
+// at once.
 #include "sol_internal.h"
 
 namespace sol {
@@ -131,26 +134,30 @@ attn_fwd_kernel(
     const int work = xcd_remap(blockIdx.x, gridDim.x, g.B * g.H * nbw);
     if (work < 0) return;
     const int bh = work / nbw;
+    const int b = bh / g.H, h = bh - b * g.H;
+    // this sample's length and blocks (all equal unless the batch is packed)
+    const Seq sq = seq_of(g, b);
     // the rank-th query block of this (batch, head) in the routing schedule
-    // (longest list first), or in sequence order without one
+    // (longest list first), or in sequence order without one; ranks past the
+    // sample's own blocks have no work
     const int rank = work - bh * nbw;
+    if (NQ * rank >= sq.NB) return;
     const int qb = DENSE ? NQ * rank
                  : order == nullptr ? rank
-                                    : min(max(order[(int64_t)bh * g.NB + rank], 0), g.NB - 1);
+                                    : min(max(order[(int64_t)bh * g.NB + rank], 0), sq.NB - 1);
     const int item = bh * g.NB + qb;
-    const int b = bh / g.H, h = bh - b * g.H;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // wave w owns rows 32 (w & 1) .. +31 of query block qb + (w >> 1); past the
     // last block (odd NB, dense) it repeats the last block, whose rows it then
     // writes with the same values as its partner waves
-    const int qrow0 = min(qb + (wave >> 1), g.NB - 1) * 64 + 32 * (wave & 1);
+    const int qrow0 = min(qb + (wave >> 1), sq.NB - 1) * 64 + 32 * (wave & 1);
     const int lane = tid & 63;
     const int l32 = lane & 31, u = lane >> 5;
 
-    const int64_t head_off = (int64_t)b * g.sb + (int64_t)h * g.sh;
+    const int64_t head_off = sq.base + (int64_t)h * g.sh;
     const uint32_t rowstride = (uint32_t)(g.sn * 2);
-    const uint32_t bound = (uint32_t)(((int64_t)(g.N - 1) * g.sn + D) * 2);
+    const uint32_t bound = (uint32_t)(((int64_t)(sq.N - 1) * g.sn + D) * 2);
     const __amdgpu_buffer_rsrc_t rq = rsrc(q + head_off, bound);
     const __amdgpu_buffer_rsrc_t rk = rsrc(k + head_off, bound);
     const __amdgpu_buffer_rsrc_t rv = rsrc(v + head_off, bound);
@@ -164,10 +171,10 @@ attn_fwd_kernel(
     }
 
     // ---- the tile walk: sink tiles, then routed blocks (list copied to LDS)
-    const int nsink = DENSE ? g.NB : (g.Ssink + 63) / 64;
+    const int nsink = DENSE ? sq.NB : (sq.Ssink + 63) / 64;
     int nlist = 0;
     if (!DENSE) {
-        nlist = min(max(cnt[item], 0), min(g.ncand, kMaxList));
+        nlist = min(max(cnt[item], 0), min(sq.ncand, kMaxList));
         if (nlist > 0) {
             // 2-byte loads: buffer range checks work per dword, so a wider load
             // would drop the last entry of an odd-length list
@@ -180,7 +187,7 @@ attn_fwd_kernel(
     __syncthreads();
     int first = 0;
     bool straddle_in = false;
-    if (!DENSE && nlist > 0 && (g.S & 63) != 0 && g.S < g.N && lst[0] == g.j0) {
+    if (!DENSE && nlist > 0 && (g.S & 63) != 0 && g.S < sq.N && lst[0] == sq.j0) {
         // the straddle block's routable keys join its (masked) sink tile
         straddle_in = true;
         first = 1;
@@ -188,12 +195,12 @@ attn_fwd_kernel(
     const int ntiles = nsink + nlist - first;
     auto tile_block = [&](int t) -> int {
         if (DENSE || t < nsink) return t;
-        return min(max((int)lst[first + t - nsink], 0), g.NB - 1);
+        return min(max((int)lst[first + t - nsink], 0), sq.NB - 1);
     };
     auto tile_kmax = [&](int t, int blk) -> int {
-        if (DENSE || t >= nsink) return min(64 * blk + 64, g.N);
+        if (DENSE || t >= nsink) return min(64 * blk + 64, sq.N);
         if (t < nsink - 1) return 64 * blk + 64;
-        return straddle_in ? min(64 * blk + 64, g.N) : g.Ssink;
+        return straddle_in ? min(64 * blk + 64, sq.N) : sq.Ssink;
     };
 
     // ---- global -> LDS half-tile loads.  Wave load n (this wave issues
@@ -434,8 +441,8 @@ attn_fwd_kernel(
     }
 
     // ---- epilogue: normalise, round to bf16, store rows < N only
-    const int64_t o_off = (int64_t)b * g.osb + (int64_t)h * g.osh;
-    const uint32_t obound = (uint32_t)(((int64_t)(g.N - 1) * g.osn + D) * 2);
+    const int64_t o_off = sq.obase + (int64_t)h * g.osh;
+    const uint32_t obound = (uint32_t)(((int64_t)(sq.N - 1) * g.osn + D) * 2);
     const __amdgpu_buffer_rsrc_t ro = rsrc(o + o_off, obound);
     const uint32_t orow = (uint32_t)(g.osn * 2);
     const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
@@ -456,7 +463,7 @@ attn_fwd_kernel(
                                                   row * orow + 2 * d0, 0, 0);
         }
     if (lse != nullptr && u == 0) {
-        const __amdgpu_buffer_rsrc_t rl = rsrc(lse + (int64_t)bh * g.N, (uint32_t)g.N * 4);
+        const __amdgpu_buffer_rsrc_t rl = rsrc(lse + (int64_t)bh * g.N, (uint32_t)sq.N * 4);
         const float val = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rl, row * 4, 0, 0);
     }

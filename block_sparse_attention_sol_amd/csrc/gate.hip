@@ -34,10 +34,11 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ 
     float mx = 0.f;
     double s_abs = 0.0, s_sq = 0.0, s_ref = 0.0;
     int n = 0;
-    if (row < g.N) {
-        for (int bh = blockIdx.y; bh < g.B * g.H; bh += gridDim.y) {
-            const int bb = bh / g.H, h = bh - bb * g.H;
-            const int64_t off = (int64_t)bb * g.osb + (int64_t)row * g.osn + (int64_t)h * g.osh;
+    for (int bh = blockIdx.y; bh < g.B * g.H; bh += gridDim.y) {
+        const int bb = bh / g.H, h = bh - bb * g.H;
+        const Seq sq = seq_of(g, bb);      // rows of a packed sample end at its own length
+        if (row < sq.N) {
+            const int64_t off = sq.obase + (int64_t)row * g.osn + (int64_t)h * g.osh;
             for (int d = lane; d < g.D; d += 64) {
                 const float x = bf16_to_f32(a[off + d]), y = bf16_to_f32(b[off + d]);
                 const float e = fabsf(x - y);
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t* __restrict__ 
         s_sq += __shfl_xor(s_sq, m, 64);
         s_ref += __shfl_xor(s_ref, m, 64);
     }
-    if (lane == 0 && row < g.N) {
+    if (lane == 0 && n > 0) {
         // non-negative floats order like their bit patterns
         atomicMax((unsigned long long*)&stats[0],
                   (unsigned long long)__double_as_longlong((double)mx));

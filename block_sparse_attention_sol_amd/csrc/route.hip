@@ -49,14 +49,16 @@ __global__ __launch_bounds__(256) void pool_kernel(
     const int chunks = g.D >> 3;
     const int lane_id = blockIdx.y * 256 + threadIdx.x;
     if (lane_id >= g.H * chunks) return;
+    const Seq sq = seq_of(g, b);
+    if (blk >= sq.NB) return;                  // past this sample's last block
     const int h = lane_id / chunks, c = lane_id - h * chunks;
     int r0 = blk * kBlock;
-    const int r1 = min(r0 + kBlock, g.N);
+    const int r1 = min(r0 + kBlock, sq.N);
     if (is_k) {
-        if (blk < g.j0) return;
+        if (blk < sq.j0) return;
         r0 = max(r0, g.S);
     }
-    const uint16_t* src = (is_k ? k : q) + (int64_t)b * g.sb + (int64_t)h * g.sh + c * 8;
+    const uint16_t* src = (is_k ? k : q) + sq.base + (int64_t)h * g.sh + c * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int t = r0;
     // rows strictly in ascending order; loads are issued 16 ahead
@@ -138,10 +140,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
     if (work < 0) return;
     const int bh = work / tiles_per_bh;
     const int i0 = (work - bh * tiles_per_bh) * TI;
-    const int ni = min(TI, g.NB - i0);
     const int W = blockDim.x >> 6;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int slots = 64 * W;
+    const Seq sq = seq_of(g, bh / g.H);
+    // query blocks of this tile inside the sample; the tile's rows past the
+    // sample's last block (packed batches) get empty lists
+    const int ni = min(TI, sq.NB - i0);
+    if (tid < min(TI, g.NB - i0) && tid >= ni) cnt[(int64_t)bh * g.NB + i0 + tid] = 0;
+    if (ni <= 0) return;
 
     __shared__ float red[TI][kMaxWaves];
     __shared__ int wcount[TI][JPL * kMaxWaves];
@@ -173,8 +180,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
 #pragma unroll
     for (int jj = 0; jj < JPL; ++jj) {
         const int s = jj * slots + tid;
-        jvalid[jj] = s < g.ncand;
-        jrow[jj] = g.j0 + (jvalid[jj] ? s : 0);
+        jvalid[jj] = s < sq.ncand;
+        // slots past the candidates read row 0 (always inside the workspace,
+        // even when the sample has no candidate) and score -inf below
+        jrow[jj] = jvalid[jj] ? sq.j0 + s : 0;
 #pragma unroll
         for (int ii = 0; ii < TI; ++ii) acc[jj][ii] = 0.f;
     }
@@ -231,15 +240,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
 #pragma unroll
     for (int ii = 0; ii < TI; ++ii) {
         const int i = i0 + ii;
-        const uint32_t rows = (uint32_t)max(min(kBlock, g.N - kBlock * i), 0);
+        const uint32_t rows = (uint32_t)max(min(kBlock, sq.N - kBlock * i), 0);
 #pragma unroll
         for (int jj = 0; jj < JPL; ++jj) {
             const int sl = jj * slots + tid;
-            const int j = g.j0 + sl;
+            const int j = sq.j0 + sl;
             const bool sel = (ii < ni) && jvalid[jj] && (sc[jj][ii] >= thr[ii] || j == i);
             const uint64_t bal = __ballot(sel);
             if (lane == 0) balls[ii][jj * W + wave] = bal;
-            const uint32_t keys = (uint32_t)(min(kBlock * j + kBlock, g.N) - max(kBlock * j, g.S));
+            const uint32_t keys = (uint32_t)(min(kBlock * j + kBlock, sq.N) - max(kBlock * j, g.S));
             keys_local += sel ? rows * keys : 0u;
         }
     }
@@ -252,9 +261,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
             run += __popcll(balls[tid][e]);
         }
         cnt[(int64_t)bh * g.NB + i0 + tid] = run;
-        const int rows = min(kBlock, g.N - kBlock * (i0 + tid));
+        const int rows = min(kBlock, sq.N - kBlock * (i0 + tid));
         atomicAdd(&wg_tot[0], (unsigned long long)run);
-        atomicAdd(&wg_tot[1], (unsigned long long)rows * g.Ssink);
+        atomicAdd(&wg_tot[1], (unsigned long long)rows * sq.Ssink);
     }
     __syncthreads();
     // pass 2: compaction into ascending lists (slot order = block order)
@@ -266,7 +275,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
         for (int jj = 0; jj < JPL; ++jj) {
             const uint64_t bal = balls[ii][jj * W + wave];
             if ((bal >> lane) & 1)
-                row[woffset[ii][jj * W + wave] + lanes_below(bal)] = (int16_t)(g.j0 + jj * slots + tid);
+                row[woffset[ii][jj * W + wave] + lanes_below(bal)] = (int16_t)(sq.j0 + jj * slots + tid);
         }
     }
     const uint32_t wsum = wave_sum(keys_local);
@@ -279,20 +288,35 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
 }
 
 // S >= N: no candidates, every list is empty, only sink pairs are attended;
-// the schedule is sequence order.
-__global__ __launch_bounds__(256) void empty_route_kernel(int32_t* __restrict__ cnt, int n, int NB,
+// the schedule is sequence order.  Workgroup 0 also sums the sink pairs of
+// every sample (rows x sink keys, per head).
+__global__ __launch_bounds__(256) void empty_route_kernel(int32_t* __restrict__ cnt, Geom g,
                                                           int64_t* __restrict__ totals,
-                                                          long long sink_pairs,
                                                           int32_t* __restrict__ order)
 {
+    const int n = g.B * g.H * g.NB;
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i < n) {
         cnt[i] = 0;
-        if (order != nullptr) order[i] = i % NB;
+        if (order != nullptr) order[i] = i % g.NB;
     }
-    if (i == 0) {
-        totals[0] = 0;
-        totals[1] = sink_pairs;
+    if (blockIdx.x == 0) {
+        __shared__ unsigned long long part[256];
+        unsigned long long acc = 0;
+        for (int b = threadIdx.x; b < g.B; b += 256) {
+            const Seq sq = seq_of(g, b);
+            acc += (unsigned long long)g.H * sq.N * sq.Ssink;
+        }
+        part[threadIdx.x] = acc;
+        __syncthreads();
+        for (int off = 128; off > 0; off >>= 1) {
+            if (threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) {
+            totals[0] = 0;
+            totals[1] = (int64_t)part[0];
+        }
     }
 }
 
@@ -303,24 +327,29 @@ __global__ __launch_bounds__(256) void empty_route_kernel(int32_t* __restrict__ 
 // ascending walks sweep the key blocks at similar rates and share them in L2.
 // Blocks of equal length keep no particular order; each query block's output
 // does not depend on the order, only the timing does.
-// grid: B * H; block: 256; dynamic LDS: ncand + 1 ints.
+// A packed sample sorts its own blocks; the row's entries past them hold
+// their own index.
+// grid: B * H; block: 256; dynamic LDS: ncand + 1 ints (ncand of the call).
 __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ cnt, Geom g,
                                                     int32_t* __restrict__ order)
 {
     extern __shared__ int hist[];          // per list length: count, then next slot
     __shared__ int part[256];
     const int tid = threadIdx.x;
-    const int nbins = g.ncand + 1;
+    const Seq sq = seq_of(g, blockIdx.x / g.H);
+    const int ncand = sq.ncand, NB = sq.NB;
+    const int nbins = ncand + 1;
     const int64_t row = (int64_t)blockIdx.x * g.NB;
+    for (int i = NB + tid; i < g.NB; i += 256) order[row + i] = i;
     for (int b = tid; b < nbins; b += 256) hist[b] = 0;
     __syncthreads();
-    for (int i = tid; i < g.NB; i += 256) atomicAdd(&hist[min(max(cnt[row + i], 0), g.ncand)], 1);
+    for (int i = tid; i < NB; i += 256) atomicAdd(&hist[min(max(cnt[row + i], 0), ncand)], 1);
     __syncthreads();
     // descending exclusive scan: thread t owns lengths ncand - k for k in its range
     const int per = (nbins + 255) / 256;
     const int k0 = min(tid * per, nbins), k1 = min(k0 + per, nbins);
     int local = 0;
-    for (int kk = k0; kk < k1; ++kk) local += hist[g.ncand - kk];
+    for (int kk = k0; kk < k1; ++kk) local += hist[ncand - kk];
     part[tid] = local;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {      // inclusive Hillis-Steele scan
@@ -331,14 +360,14 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
     }
     int run = part[tid] - local;
     for (int kk = k0; kk < k1; ++kk) {
-        const int b = g.ncand - kk;
+        const int b = ncand - kk;
         const int n = hist[b];
         hist[b] = run;
         run += n;
     }
     __syncthreads();
-    for (int i = tid; i < g.NB; i += 256) {
-        const int pos = atomicAdd(&hist[min(max(cnt[row + i], 0), g.ncand)], 1);
+    for (int i = tid; i < NB; i += 256) {
+        const int pos = atomicAdd(&hist[min(max(cnt[row + i], 0), ncand)], 1);
         order[row + pos] = i;
     }
 }
@@ -381,9 +410,8 @@ hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale
 {
     if (g.ncand == 0) {
         const int n = g.B * g.H * g.NB;
-        const long long pairs = (long long)g.B * g.H * g.N * g.Ssink;
-        hipLaunchKernelGGL(empty_route_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cnt, n,
-                           g.NB, totals, pairs, order);
+        hipLaunchKernelGGL(empty_route_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cnt, g,
+                           totals, order);
         return hipGetLastError();
     }
     const size_t one = ((size_t)g.B * g.H * g.NB * g.D + 63) / 64 * 64;

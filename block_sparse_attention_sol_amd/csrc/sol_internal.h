@@ -20,7 +20,43 @@ struct Geom {
     int ncand;     // NB - j0
     int64_t sb, sn, sh;      // Q/K/V element strides
     int64_t osb, osn, osh;   // O element strides
+    const int32_t* cu;       // packed variable-length batch: B + 1 row offsets (device), or null
+    int64_t T;               // rows of the packed tensors (with cu only)
 };
+
+// Geometry of sample b.  A fixed-length batch gives every sample the call's N
+// at offset b * sb.  A packed variable-length batch reads the sample's rows
+// [cu[b], cu[b + 1]) from the offsets, clamped so that the sample stays
+// inside [0, T) and holds at most N rows: no access can leave the buffers,
+// whatever the offsets hold.  The rest follows from the sample's own length
+// exactly as on the host: its blocks, sink, first candidate and candidates.
+struct Seq {
+    int64_t base;    // element offset of the sample's row 0 in Q, K and V
+    int64_t obase;   // element offset of the sample's row 0 in O
+    int N, NB, Ssink, j0, ncand;
+};
+
+__device__ __forceinline__ Seq seq_of(const Geom& g, int b) {
+    Seq s;
+    int n;
+    if (g.cu == nullptr) {
+        n = g.N;
+        s.base = (int64_t)b * g.sb;
+        s.obase = (int64_t)b * g.osb;
+    } else {
+        const int64_t start = min(max((int64_t)g.cu[b], (int64_t)0), g.T);
+        const int64_t end = min(max((int64_t)g.cu[b + 1], start), min(g.T, start + g.N));
+        n = (int)(end - start);
+        s.base = start * g.sn;
+        s.obase = start * g.osn;
+    }
+    s.N = n;
+    s.NB = (n + kBlock - 1) / kBlock;
+    s.Ssink = min(g.S, n);
+    s.j0 = g.S >= n ? s.NB : g.S / kBlock;
+    s.ncand = s.NB - s.j0;
+    return s;
+}
 
 // Workgroup id -> logical work index, so that consecutive logical indices
 // (same head) land on the same XCD and share its L2.  The grid must be a

@@ -31,7 +31,8 @@ class Desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("N", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("D", ctypes.c_int32),
                 ("qkv_sb", ctypes.c_int64), ("qkv_sn", ctypes.c_int64), ("qkv_sh", ctypes.c_int64),
-                ("o_sb", ctypes.c_int64), ("o_sn", ctypes.c_int64), ("o_sh", ctypes.c_int64)]
+                ("o_sb", ctypes.c_int64), ("o_sn", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+                ("cu_seqlens", ctypes.c_void_p), ("total_rows", ctypes.c_int64)]
 
 
 def _load():
@@ -76,15 +77,49 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def make_desc(q: torch.Tensor, o: torch.Tensor | None = None) -> Desc:
-    """Descriptor of [B, N, H, D] bf16 tensors: Q/K/V strides from q, O strides from o."""
-    if q.dim() != 4:
-        raise ValueError("expected [B, N, H, D] tensors")
-    B, N, H, D = q.shape
+def packed_offsets(lengths, device) -> tuple[torch.Tensor, int]:
+    """Row offsets (int32 [B + 1] on `device`) and the longest length of a packed
+    variable-length batch whose samples have the given lengths."""
+    lengths = [int(n) for n in lengths]
+    if not lengths or min(lengths) < 0:
+        raise ValueError("need one or more non-negative sample lengths")
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + n)
+    return torch.tensor(cu, dtype=torch.int32, device=device), max(max(lengths), 1)
+
+
+def _shape(q: torch.Tensor, cu_seqlens, max_seqlen):
+    """(B, N, H, D) of a call: from [B, N, H, D] tensors, or from packed [T, H, D]
+    tensors with row offsets cu_seqlens (N = max_seqlen, the longest sample)."""
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("expected [B, N, H, D] tensors")
+        return tuple(q.shape)
+    if q.dim() != 3:
+        raise ValueError("a packed batch takes [T, H, D] tensors")
+    if (cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2 or cu_seqlens.dtype != torch.int32
+            or cu_seqlens.device != q.device):
+        raise ValueError("cu_seqlens must be int32 [B + 1] on the tensors' device")
+    if max_seqlen is None or int(max_seqlen) < 1:
+        raise ValueError("a packed batch needs max_seqlen >= 1 (the longest sample)")
+    T, H, D = q.shape
+    return cu_seqlens.numel() - 1, int(max_seqlen), H, D
+
+
+def make_desc(q: torch.Tensor, o: torch.Tensor | None = None, cu_seqlens=None,
+              max_seqlen=None) -> Desc:
+    """Descriptor of [B, N, H, D] bf16 tensors (or packed [T, H, D] ones with row
+    offsets cu_seqlens): Q/K/V strides from q, O strides from o."""
+    B, N, H, D = _shape(q, cu_seqlens, max_seqlen)
     o = q if o is None else o
-    if q.stride(3) != 1 or o.stride(3) != 1:
+    if q.stride(-1) != 1 or o.stride(-1) != 1:
         raise SolError(SOL_ERR_UNSUPPORTED, "stride along D must be 1")
-    return Desc(B, N, H, D, q.stride(0), q.stride(1), q.stride(2), o.stride(0), o.stride(1), o.stride(2))
+    if cu_seqlens is None:
+        return Desc(B, N, H, D, q.stride(0), q.stride(1), q.stride(2), o.stride(0), o.stride(1),
+                    o.stride(2), None, 0)
+    return Desc(B, N, H, D, 0, q.stride(0), q.stride(1), 0, o.stride(0), o.stride(1),
+                cu_seqlens.data_ptr(), q.shape[0])
 
 
 def _check_qkv(q, k, v=None):
@@ -96,13 +131,14 @@ def _check_qkv(q, k, v=None):
             raise ValueError("Q, K, V must share shape and strides")
 
 
-def route_workspace_bytes(q: torch.Tensor) -> int:
-    return int(lib.sol_route_workspace_bytes(ctypes.byref(make_desc(q))))
+def route_workspace_bytes(q: torch.Tensor, cu_seqlens=None, max_seqlen=None) -> int:
+    return int(lib.sol_route_workspace_bytes(ctypes.byref(make_desc(q, None, cu_seqlens,
+                                                                    max_seqlen))))
 
 
-def route_outputs(q: torch.Tensor):
+def route_outputs(q: torch.Tensor, cu_seqlens=None, max_seqlen=None):
     """Empty (blk_idx, blk_cnt, totals, order) tensors for route() on q's shape."""
-    B, N, H, D = q.shape
+    B, N, H, D = _shape(q, cu_seqlens, max_seqlen)
     NB = num_blocks(N)
     return (torch.empty((B, H, NB, NB), dtype=torch.int16, device=q.device),
             torch.empty((B, H, NB), dtype=torch.int32, device=q.device),
@@ -111,13 +147,15 @@ def route_outputs(q: torch.Tensor):
 
 
 def route(q: torch.Tensor, k: torch.Tensor, tau: float, sink: int, scale: float = 0.0,
-          workspace: torch.Tensor | None = None, out=None):
+          workspace: torch.Tensor | None = None, out=None, cu_seqlens=None, max_seqlen=None):
     """Online block routing.  Returns (blk_idx int16 [B,H,NB,NB], blk_cnt int32 [B,H,NB],
     totals int64 [2], order int32 [B,H,NB]) on q's device; only the first blk_cnt entries
-    of each row of blk_idx are set; order is the attention schedule (longest list first)."""
+    of each row of blk_idx are set; order is the attention schedule (longest list first).
+    With cu_seqlens, q and k are packed [T, H, D] and N is max_seqlen."""
     _check_qkv(q, k)
-    desc = make_desc(q)
-    idx, cnt, totals, order = route_outputs(q) if out is None else out
+    desc = make_desc(q, None, cu_seqlens, max_seqlen)
+    idx, cnt, totals, order = (route_outputs(q, cu_seqlens, max_seqlen) if out is None
+                               else out)
     need = int(lib.sol_route_workspace_bytes(ctypes.byref(desc)))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -129,19 +167,32 @@ def route(q: torch.Tensor, k: torch.Tensor, tau: float, sink: int, scale: float 
     return idx, cnt, totals, order
 
 
+def _lse_buffer(q, B, H, N, return_lse, lse_out):
+    if lse_out is not None:
+        if (lse_out.dtype != torch.float32 or tuple(lse_out.shape) != (B, H, N)
+                or not lse_out.is_contiguous() or lse_out.device != q.device):
+            raise ValueError("lse_out must be a contiguous float32 [B, H, N] tensor")
+        return lse_out
+    return torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+
+
 def attn(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, out=None, return_lse=False,
-         order=None):
-    """Sink + routed block-sparse attention forward.  Returns O (and LSE [B,H,N] fp32).
-    ``order`` is the schedule from route() (None: sequence order; results are the same)."""
+         order=None, cu_seqlens=None, max_seqlen=None, lse_out=None):
+    """Sink + routed block-sparse attention forward.  Returns O (and LSE [B,H,N] fp32,
+    into ``lse_out`` when given).  ``order`` is the schedule from route() (None:
+    sequence order; results are the same).  With cu_seqlens the tensors are
+    packed [T, H, D] and N is max_seqlen."""
     _check_qkv(q, k, v)
-    B, N, H, D = q.shape
+    B, N, H, D = _shape(q, cu_seqlens, max_seqlen)
     o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    lse = _lse_buffer(q, B, H, N, return_lse, lse_out)
+    return_lse = lse is not None
     if blk_idx.dtype != torch.int16 or blk_cnt.dtype != torch.int32:
         raise ValueError("blk_idx must be int16 and blk_cnt int32")
     if order is not None and (order.dtype != torch.int32 or order.shape != blk_cnt.shape):
         raise ValueError("order must be int32 with blk_cnt's shape")
-    st = lib.sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(make_desc(q, o)),
+    desc = make_desc(q, o, cu_seqlens, max_seqlen)
+    st = lib.sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(desc),
                           blk_idx.data_ptr(), blk_cnt.data_ptr(),
                           order.data_ptr() if order is not None else None, int(sink),
                           ctypes.c_float(scale),
@@ -150,26 +201,31 @@ def attn(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, out=None, ret
     return (o, lse) if return_lse else o
 
 
-def attn_dense(q, k, v, scale: float = 0.0, out=None, return_lse=False):
+def attn_dense(q, k, v, scale: float = 0.0, out=None, return_lse=False, cu_seqlens=None,
+               max_seqlen=None, lse_out=None):
     """Full softmax attention (routing disabled)."""
     _check_qkv(q, k, v)
-    B, N, H, D = q.shape
+    B, N, H, D = _shape(q, cu_seqlens, max_seqlen)
     o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    lse = _lse_buffer(q, B, H, N, return_lse, lse_out)
+    return_lse = lse is not None
+    desc = make_desc(q, o, cu_seqlens, max_seqlen)
     st = lib.sol_attn_dense_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                ctypes.byref(make_desc(q, o)), ctypes.c_float(scale), o.data_ptr(),
+                                ctypes.byref(desc), ctypes.c_float(scale), o.data_ptr(),
                                 lse.data_ptr() if lse is not None else None, _stream(q))
     _check(st, "sol_attn_dense_fwd")
     return (o, lse) if return_lse else o
 
 
-def gate(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, order=None):
+def gate(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, order=None, cu_seqlens=None,
+         max_seqlen=None):
     """Sparse-vs-dense gate: returns (o_sparse, o_dense, stats) with stats a float64
     tensor [max_abs, sum_abs, sum_sq_diff, sum_sq_dense, count] on q's device."""
     _check_qkv(q, k, v)
     o_s, o_d = torch.empty_like(q), torch.empty_like(q)
     stats = torch.empty(5, dtype=torch.float64, device=q.device)
-    st = lib.sol_gate_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(make_desc(q, o_s)),
+    desc = make_desc(q, o_s, cu_seqlens, max_seqlen)
+    st = lib.sol_gate_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(desc),
                           blk_idx.data_ptr(), blk_cnt.data_ptr(),
                           order.data_ptr() if order is not None else None, int(sink),
                           ctypes.c_float(scale), o_s.data_ptr(), o_d.data_ptr(), stats.data_ptr(),
@@ -185,10 +241,13 @@ def gate_summary(stats) -> dict:
             "l2_rel": math.sqrt(s[2] / s[3]) if s[3] > 0 else 0.0}
 
 
-def forward(q, k, v, tau: float, sink: int, scale: float = 0.0, return_lse=False):
+def forward(q, k, v, tau: float, sink: int, scale: float = 0.0, return_lse=False,
+            cu_seqlens=None, max_seqlen=None):
     """Routing then sparse attention on the current stream; returns (O, [LSE,] idx, cnt, totals)."""
-    idx, cnt, totals, order = route(q, k, tau, sink, scale)
-    res = attn(q, k, v, idx, cnt, sink, scale, return_lse=return_lse, order=order)
+    idx, cnt, totals, order = route(q, k, tau, sink, scale, cu_seqlens=cu_seqlens,
+                                    max_seqlen=max_seqlen)
+    res = attn(q, k, v, idx, cnt, sink, scale, return_lse=return_lse, order=order,
+               cu_seqlens=cu_seqlens, max_seqlen=max_seqlen)
     if return_lse:
         return res[0], res[1], idx, cnt, totals
     return res, idx, cnt, totals

@@ -47,6 +47,26 @@
  *     by the three tensors (they may be views of one merged QKV projection)
  *     and unit stride along D; O has its own strides.  Rows >= N are never
  *     read (loads past them return zero) and never written.
+ *   - Packed variable-length batches (mixed prompt lengths in one call;
+ *     tokenfactory.fast post, "The benchmark was not the product": served
+ *     traffic mixes prompt lengths, and one build must serve them all): when
+ *     desc->cu_seqlens is not NULL, the B samples lie back to back in
+ *     [T, H, D] tensors, T = desc->total_rows.  Sample b is rows
+ *     cu_seqlens[b] .. cu_seqlens[b + 1] - 1, its length n_b between 0 and N
+ *     (N is then the longest sample), and every rule above applies to each
+ *     sample on its own with N = n_b: its own blocks, sink, candidates and
+ *     routing, and no attention across samples.  qkv_sb and o_sb must be 0.
+ *     Per-block and per-row outputs keep the fixed-length layout, sized by
+ *     the longest sample: blk_idx [B, H, NB, NB], blk_cnt and order
+ *     [B, H, NB], lse [B, H, N] with NB = ceil(N / 64).  Past a sample's own
+ *     blocks blk_cnt is 0 and order holds the block's own index; lse rows
+ *     >= n_b and O rows outside every sample are never written.
+ *     cu_seqlens is device int32 [B + 1], non-decreasing, cu_seqlens[B] <=
+ *     T, total_rows < 2^31.  The kernels clamp each sample to [0, T) and to
+ *     at most N rows, so offsets that break these rules cannot make an
+ *     access leave the buffers (the results of such samples are then
+ *     unspecified).  A NULL cu_seqlens gives the fixed-length batch above
+ *     and total_rows is ignored.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream) and never synchronise the host.
  *   - Errors come back as a status code; nothing is printed.  Argument checks
@@ -71,7 +91,8 @@ extern "C" {
 
 typedef enum {
     SOL_OK = 0,
-    SOL_ERR_ARG = 1,          /* null pointer, non-positive size, negative S, NaN or negative tau */
+    SOL_ERR_ARG = 1,          /* null pointer, non-positive size, negative S, NaN or negative tau,
+                                 nonzero batch stride or negative T with cu_seqlens               */
     SOL_ERR_UNSUPPORTED = 2,  /* D not 64/128, stride along D != 1, a size beyond the limits    */
     SOL_ERR_ALIGN = 3,        /* a pointer or stride that breaks 16-byte row alignment          */
     SOL_ERR_WORKSPACE = 4,    /* workspace null or smaller than sol_route_workspace_bytes()     */
@@ -82,6 +103,9 @@ typedef struct {
     int32_t B, N, H, D;               /* batch, true sequence length, heads, head width    */
     int64_t qkv_sb, qkv_sn, qkv_sh;   /* element strides of Q, K and V (unit along D)      */
     int64_t o_sb, o_sn, o_sh;         /* element strides of O (unit along D)               */
+    const int32_t* cu_seqlens;        /* packed variable-length batch: device int32 [B+1]
+                                         row offsets of the samples, or NULL (fixed N)     */
+    int64_t total_rows;               /* T, rows of the packed tensors (with cu_seqlens)   */
 } sol_desc;
 
 /* Number of 64-token blocks, ceil(N / 64) (0 for N <= 0). */
@@ -130,7 +154,9 @@ sol_status sol_route(const void* q, const void* k, const sol_desc* desc, float t
  *   blk_idx,  the lists written by sol_route for the same B, N, H and
  *   blk_cnt   sink_len (entries must be ascending candidates in [j0, NB)).
  *   order     optional (NULL: sequence order) schedule written by sol_route;
- *             each row must be a permutation of 0..NB-1.  Query blocks of one
+ *             each row must be a permutation of 0..NB-1 (for a
+ *             packed sample: its first ceil(n_b / 64) entries a permutation
+ *             of its own blocks, as sol_route writes them).  Query blocks of one
  *             (batch, head) are processed in this order; results do not
  *             depend on it.
  *   sink_len  S >= 0 as for sol_route.

@@ -351,3 +351,53 @@ def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float | 
     g = geometry(N, N)                   # everything is sink: one dense softmax
     sel = np.zeros((B, H, g.NB, g.NB), bool)
     return attention(q, k, v, sel, g, scale, blocks)
+
+
+# --------------------------------------------------------------------------- packed batches
+# Several prompts of different lengths in one call (tokenfactory.fast post,
+# "The benchmark was not the product": served traffic mixes prompt lengths).
+# The pages run one prompt per forward, so the reading taken for a batch is
+# the plainest one: its samples are independent sequences.  Each has its own
+# 64-token blocks, its own sink (its first S tokens), its own candidates and
+# routing, and no query attends to another sample's keys.  The samples lie back
+# to back in [T, H, D] arrays; sample b is rows cu[b] .. cu[b + 1] - 1.
+
+def split_packed(x: np.ndarray, cu) -> list[np.ndarray]:
+    """The samples of a packed [T, H, D] array as [1, n_b, H, D] arrays."""
+    cu = [int(c) for c in cu]
+    return [x[None, cu[b]:cu[b + 1]] for b in range(len(cu) - 1)]
+
+
+def route_packed(q32: np.ndarray, k32: np.ndarray, cu, S: int, tau: float,
+                 scale32: np.float32 | None = None) -> list[Route | None]:
+    """Routing of each sample on its own (None for an empty sample)."""
+    out = []
+    for qs, ks in zip(split_packed(q32, cu), split_packed(k32, cu)):
+        n = qs.shape[1]
+        out.append(route(qs, ks, n, S, tau, scale32) if n > 0 else None)
+    return out
+
+
+def attention_packed(q: np.ndarray, k: np.ndarray, v: np.ndarray, routes, cu,
+                     scale: float | None = None, dense: bool = False):
+    """Sink + routed (or, with ``dense``, full) attention of each sample, float64.
+
+    Returns (O [T, H, D] with NaN on rows outside every sample, [L_b [H, n_b]]).
+    """
+    T, H, D = q.shape
+    O = np.full((T, H, D), np.nan)
+    Ls = []
+    cu = [int(c) for c in cu]
+    for b, (qs, ks, vs) in enumerate(zip(split_packed(q, cu), split_packed(k, cu),
+                                         split_packed(v, cu))):
+        n = qs.shape[1]
+        if n == 0:
+            Ls.append(np.zeros((H, 0)))
+            continue
+        if dense:
+            o, lse = dense_attention(qs, ks, vs, scale)
+        else:
+            o, lse = attention(qs, ks, vs, routes[b].sel, routes[b].geom, scale)
+        O[cu[b]:cu[b + 1]] = o[0]
+        Ls.append(lse[0])
+    return O, Ls

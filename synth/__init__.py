@@ -210,3 +210,25 @@ def make_qkv(w: Workload, heads: list[int] | None = None, threads: int = 8):
         for j in jobs:
             one(j)
     return out[0], out[1], out[2]
+
+
+def packed_batch(calls: list[Workload], threads: int = 8):
+    """Several workloads (same H and D, B = 1 each) as one packed batch.
+
+    Returns (q, k, v, cu): bf16 bit patterns [T, H, D] with the samples back to
+    back in the order given, and the row offsets cu (int64 [len(calls) + 1]).
+    Each sample holds exactly the values make_qkv draws for its workload.
+    """
+    if not calls or any(c.B != 1 or c.H != calls[0].H or c.D != calls[0].D for c in calls):
+        raise ValueError("packed samples need B = 1 and one H and D")
+    lengths = [c.N if c.N > 0 else 0 for c in calls]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T, H, D = int(cu[-1]), calls[0].H, calls[0].D
+    out = [np.empty((T, H, D), dtype=np.uint16) for _ in range(3)]
+    for c, s0, s1 in zip(calls, cu[:-1], cu[1:]):
+        if s1 == s0:
+            continue
+        for t, x in enumerate(make_qkv(c, threads=threads)):
+            out[t][s0:s1] = x[0]
+    return out[0], out[1], out[2], cu
+

@@ -52,6 +52,17 @@ def gpu_lists_to_mask(idx: np.ndarray, cnt: np.ndarray, NB: int) -> np.ndarray:
     return sel
 
 
+def check_schedule(order, cnt):
+    """Each row of the schedule is a permutation of the query blocks with
+    non-increasing list length (ties may come in any order)."""
+    B, H, NB = cnt.shape
+    for b in range(B):
+        for h in range(H):
+            o = order[b, h].astype(np.int64)
+            assert np.array_equal(np.sort(o), np.arange(NB)), (b, h)
+            assert np.all(np.diff(cnt[b, h][o]) <= 0), (b, h)
+
+
 def compare_masks(gpu_sel: np.ndarray, r: orc.Route) -> None:
     """Bit-exact mask parity; a mismatch is allowed only on a listed near-tie."""
     diff = np.argwhere(gpu_sel != r.sel)

@@ -65,6 +65,14 @@ def _desc(lib, B=1, N=1000, H=2, D=128, sn=None, sh=None, sb=None):
     return lib.Desc(B, N, H, D, sb, sn, sh, sb, sn, sh)
 
 
+def _packed_desc(lib, B=3, N=1000, H=2, D=128, T=2000, cu=0x90000, sb=0, osb=0):
+    """Packed variable-length batch: [T, H, D] tensors with row offsets at `cu`."""
+    d = lib.Desc(B, N, H, D, sb, H * D, D, osb, H * D, D)
+    d.cu_seqlens = cu
+    d.total_rows = T
+    return d
+
+
 def _route(lib, desc, q=0x10000, k=0x20000, tau=1.0, sink=64, scale=0.0, idx=0x30000,
            cnt=0x40000, tot=0x50000, order=None, ws=0x60000, ws_bytes=None):
     if ws_bytes is None:
@@ -91,6 +99,8 @@ def test_workspace_size(lib):
     ("nan_tau", 1), ("negative_tau", 1), ("nan_scale", 1), ("misaligned_q", 3),
     ("odd_stride", 3), ("small_workspace", 4), ("null_workspace", 4), ("misaligned_ws", 3),
     ("misaligned_order", 3), ("too_many_blocks", 2), ("huge_span", 2),
+    ("packed_batch_stride", 1), ("packed_out_batch_stride", 1), ("packed_negative_rows", 1),
+    ("packed_too_many_rows", 2), ("packed_misaligned_offsets", 3),
 ])
 def test_route_argument_errors(lib, case, expect):
     d = _desc(lib)
@@ -130,12 +140,23 @@ def test_route_argument_errors(lib, case, expect):
         d = _desc(lib, N=64 * 5000, H=1)          # 5000 candidate blocks > 4096
     elif case == "huge_span":
         d = _desc(lib, N=1 << 20, H=64, D=128)    # 32-bit per-head byte window exceeded
+    elif case == "packed_batch_stride":
+        d = _packed_desc(lib, sb=256000)          # packed rows take no batch stride
+    elif case == "packed_out_batch_stride":
+        d = _packed_desc(lib, osb=256000)
+    elif case == "packed_negative_rows":
+        d = _packed_desc(lib, T=-1)
+    elif case == "packed_too_many_rows":
+        d = _packed_desc(lib, T=1 << 31)          # offsets are int32
+    elif case == "packed_misaligned_offsets":
+        d = _packed_desc(lib, cu=0x90002)
     assert _route(lib, d, **kw) == expect
 
 
 @pytest.mark.parametrize("case,expect", [
     ("D32", 2), ("null_v", 1), ("null_idx", 1), ("misaligned_o", 3), ("misaligned_lse", 3),
     ("negative_scale", 1), ("inf_scale", 1), ("odd_o_stride", 3), ("misaligned_order", 3),
+    ("packed_batch_stride", 1), ("packed_misaligned_offsets", 3),
 ])
 def test_attention_argument_errors(lib, case, expect):
     d = _desc(lib)
@@ -158,6 +179,10 @@ def test_attention_argument_errors(lib, case, expect):
         d = lib.Desc(1, 1000, 2, 128, 256000, 256, 128, 256000, 260, 128)
     elif case == "misaligned_order":
         kw["order"] = 0x70002
+    elif case == "packed_batch_stride":
+        d = _packed_desc(lib, sb=256000)
+    elif case == "packed_misaligned_offsets":
+        d = _packed_desc(lib, cu=0x90001)
     assert _attn(lib, d, **kw) == expect
 
 
@@ -189,3 +214,5 @@ def test_gate_argument_errors(lib):
     assert gate(stats=0x80004) == 3         # float64 statistics need 8-byte alignment
     assert gate(od=0x70002) == 3
     assert gate(sink=-1) == 1
+    d = _packed_desc(lib, osb=1024)
+    assert gate() == 1                      # a packed batch takes no output batch stride

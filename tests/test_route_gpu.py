@@ -14,7 +14,7 @@ import pytest
 
 import synth
 from oracle import oracle as orc
-from tests.helpers import compare_masks, gpu_lists_to_mask, log, to_dev
+from tests.helpers import check_schedule, compare_masks, gpu_lists_to_mask, log, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -46,17 +46,6 @@ def _route_and_check(sol, q_bits, k_bits, N, S, tau, what):
     log(f"{what}: routed {dens['route'][0]}/{dens['route'][1]} "
         f"({dens['route'][0] / max(dens['route'][1], 1):.4%}), pairs {int(totals[1])}")
     return r
-
-
-def check_schedule(order, cnt):
-    """Each row of the schedule is a permutation of the query blocks with
-    non-increasing list length (ties may come in any order)."""
-    B, H, NB = cnt.shape
-    for b in range(B):
-        for h in range(H):
-            o = order[b, h].astype(np.int64)
-            assert np.array_equal(np.sort(o), np.arange(NB)), (b, h)
-            assert np.all(np.diff(cnt[b, h][o]) <= 0), (b, h)
 
 
 @pytest.mark.parametrize("name", ["tiny", "mid"])
