@@ -138,7 +138,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="page", choices=["page", "page_dense", "mid"])
+    ap.add_argument("--workload", default="page",
+                    choices=["page", "page_dense", "mid", "varlen_packed"],
+                    help="varlen_packed: the 16 variable-length prompts (N in [36000, 40000], "
+                         "H = 14) packed into one call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2048)
     ap.add_argument("--cpu-heads", type=int, default=4)
@@ -179,28 +182,42 @@ def main() -> int:
     import block_sparse_attention_sol_amd as sol
     import synth
 
-    w = synth.WORKLOADS[args.workload]
-    dense = w.dense
-    t0 = time.perf_counter()
-    q_bits, k_bits, v_bits = synth.make_qkv(w)
-    err(f"generated {w.name} inputs in {time.perf_counter() - t0:.1f} s")
+    packed = args.workload == "varlen_packed"
     dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    if packed:
+        # one packed batch: the samples back to back in [T, H, D], rows through offsets
+        calls = synth.varlen_calls()
+        w = calls[0]
+        q_bits, k_bits, v_bits, cu_h = synth.packed_batch(calls)
+        lengths = [int(n) for n in np.diff(cu_h)]
+        B, N, H, D = len(calls), max(lengths), w.H, w.D
+    else:
+        w = synth.WORKLOADS[args.workload]
+        q_bits, k_bits, v_bits = synth.make_qkv(w)
+        B, N, H, D = w.B, w.N, w.H, w.D
+        lengths = [N] * B
+    dense = w.dense
+    err(f"generated {args.workload} inputs in {time.perf_counter() - t0:.1f} s")
 
     def to_dev(b):
         return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
 
     q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    vk = {}
+    if packed:
+        vk = {"cu_seqlens": torch.tensor(np.asarray(cu_h, np.int32), device=dev), "max_seqlen": N}
     o = torch.empty_like(q)
-    ws = torch.empty(max(sol.route_workspace_bytes(q), 256), dtype=torch.uint8, device=dev)
-    outs = sol.route_outputs(q)
+    ws = torch.empty(max(sol.route_workspace_bytes(q, **vk), 256), dtype=torch.uint8, device=dev)
+    outs = sol.route_outputs(q, **vk)
     idx, cnt, totals, order = outs
 
     def step():
         if dense:
-            sol.attn_dense(q, k, v, out=o)
+            sol.attn_dense(q, k, v, out=o, **vk)
         else:
-            sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs)
-            sol.attn(q, k, v, idx, cnt, w.sink, out=o, order=order)
+            sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs, **vk)
+            sol.attn(q, k, v, idx, cnt, w.sink, out=o, order=order, **vk)
 
     for _ in range(args.warmup):
         step()
@@ -215,12 +232,12 @@ def main() -> int:
     for s in range(args.steps):
         ev[s][0].record()
         if not dense:
-            sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs)
+            sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs, **vk)
         ev[s][1].record()
         if dense:
-            sol.attn_dense(q, k, v, out=o)
+            sol.attn_dense(q, k, v, out=o, **vk)
         else:
-            sol.attn(q, k, v, idx, cnt, w.sink, out=o, order=order)
+            sol.attn(q, k, v, idx, cnt, w.sink, out=o, order=order, **vk)
         ev[s][2].record()
     end.record()
     torch.cuda.synchronize()
@@ -230,33 +247,66 @@ def main() -> int:
     attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
     t_route = float(np.mean(route_ms)) if not dense else 0.0
     t_attn = float(np.mean(attn_ms))
+    sep_ms = None
+    if packed:
+        # the same prompts as one fixed-length call each, for comparison
+        views = [tuple(x[int(a):int(b)].unsqueeze(0) for x in (q, k, v))
+                 for a, b in zip(cu_h[:-1], cu_h[1:])]
+        sep_out = [sol.route_outputs(vw[0]) for vw in views]
+        sep_o = [torch.empty_like(vw[0]) for vw in views]
 
-    B, N, H, D = w.B, w.N, w.H, w.D
+        def separate():
+            for (qs, ks, vs), so, oo in zip(views, sep_out, sep_o):
+                sol.route(qs, ks, w.tau, w.sink, workspace=ws, out=so)
+                sol.attn(qs, ks, vs, so[0], so[1], w.sink, out=oo, order=so[3])
+        separate()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            separate()
+        s1.record()
+        torch.cuda.synchronize()
+        sep_ms = s0.elapsed_time(s1) / args.steps
+
     NB = sol.num_blocks(N)
-    Ssink = min(w.sink, N)
+    # per-sample blocks and candidates (all equal unless the batch is packed)
+    nbs = [sol.num_blocks(n) for n in lengths]
+    ncands = [nb - (nb if w.sink >= n else w.sink // 64) for n, nb in zip(lengths, nbs)]
     if dense:
-        pairs = B * H * N * N
-        routed = B * H * NB * NB
-        ncand = NB
+        pairs = H * sum(n * n for n in lengths)
+        routed = H * sum(nb * nb for nb in nbs)
+        cand_pairs = routed
     else:
         tot = totals.cpu().numpy()
         routed, pairs = int(tot[0]), int(tot[1])
-        ncand = NB - (NB if w.sink >= N else w.sink // 64)
+        cand_pairs = H * sum(nb * nc for nb, nc in zip(nbs, ncands))
     flop_eff = 4.0 * D * pairs
-    rho_route = routed / (B * H * NB * ncand)
-    rho_pair = pairs / (B * H * N * N)
+    rho_route = routed / cand_pairs
+    rho_pair = pairs / (H * sum(n * n for n in lengths))
     tflops = flop_eff / (ms_step * 1e-3) / 1e12
     attn_tflops = flop_eff / (t_attn * 1e-3) / 1e12
-    route_bytes = (B * N * H * D * 2 + B * max(N - Ssink, 0) * H * D * 2
+    route_bytes = (sum(n * H * D * 2 + max(n - w.sink, 0) * H * D * 2 for n in lengths)
                    + 2 * routed + 4 * B * H * NB + 16) if not dense else 0
     route_gbs = route_bytes / (t_route * 1e-3) / 1e9 if not dense else None
-    err(f"{w.name}: {ms_step:.3f} ms/forward (route {t_route:.3f} ms, attention {t_attn:.3f} ms), "
+    err(f"{args.workload}: {ms_step:.3f} ms/forward (route {t_route:.3f} ms, attention {t_attn:.3f} ms), "
         f"effective {tflops:.1f} TFLOP/s, attention {attn_tflops:.1f} TFLOP/s "
         f"({attn_tflops / PEAK_BF16_TFLOPS:.1%} of bf16 peak), routing "
         f"{(route_gbs or 0):.0f} GB/s; route density {rho_route:.4%}, pair density {rho_pair:.4%}; "
         f"wall {wall:.2f} s for {args.steps} steps")
 
-    traffic = measured_traffic()
+    # the committed counter runs cover the pages' sparse shape only
+    traffic = measured_traffic() if args.workload == "page" else None
+    if packed:
+        desc = (f"varlen_packed: one Sol-Attn forward (routing + sink/routed attention) of "
+                f"{B} prompts with N in [{min(lengths)}, {max(lengths)}] packed in one call "
+                f"([{sum(lengths)},{H},{D}] bf16 with row offsets), sink {w.sink}, 64-token "
+                f"blocks, tau {w.tau}")
+    elif dense:
+        desc = f"{w.name}: dense attention (routing disabled) on [{B},{N},{H},{D}] bf16"
+    else:
+        desc = (f"{w.name}: one Sol-Attn forward (routing + sink/routed attention) on "
+                f"[{B},{N},{H},{D}] bf16, sink {w.sink}, 64-token blocks, tau {w.tau}")
     rec = {
         "metric": "ms/forward + effective TFLOP/s (MFMA % peak) at [1,38247,56,128], ~19% density",
         "value": round(tflops, 2),
@@ -271,10 +321,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (f"{w.name}: one Sol-Attn forward (routing + sink/routed attention) on "
-                         f"[{B},{N},{H},{D}] bf16, sink {w.sink}, 64-token blocks, tau {w.tau}"
-                         if not dense else
-                         f"{w.name}: dense attention (routing disabled) on [{B},{N},{H},{D}] bf16"),
+            "workload": desc,
             "B": B, "N": N, "H": H, "D": D, "sink": w.sink, "tau": w.tau,
             "route_density": round(rho_route, 6), "pair_density": round(rho_pair, 6),
             "routed_block_pairs": routed, "attended_pairs": pairs,
@@ -291,11 +338,17 @@ def main() -> int:
             "traffic": traffic,
         },
     }
-    if not args.no_cpu_baseline:
+    if packed and not args.no_cpu_baseline:
+        err("cpu baseline: timed on the default (pages' shape) workload only")
+    if not args.no_cpu_baseline and not packed:
         t0 = time.perf_counter()
         rec["cpu_baseline"] = cpu_baseline(w, q_bits, k_bits, v_bits, args.cpu_heads, args.cpu_blocks,
                                            flop_eff)
         err(f"cpu baseline took {time.perf_counter() - t0:.1f} s")
+    if packed:
+        rec["config"]["sample_lengths"] = lengths
+        rec["config"]["separate_calls_ms"] = round(sep_ms, 4)
+        err(f"the same {B} prompts as separate calls: {sep_ms:.3f} ms per forward")
     print(json.dumps(rec), flush=True)
     return 0
 
