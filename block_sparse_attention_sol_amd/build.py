@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsol.so")
-SOURCES = ["api.cpp", "route.hip", "attn.hip", "gate.hip"]
+SOURCES = ["api.cpp", "route.hip", "attn.hip", "gate.hip", "qknorm.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

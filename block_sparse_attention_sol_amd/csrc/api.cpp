@@ -157,6 +157,61 @@ sol_status sol_gate_fwd(const void* q, const void* k, const void* v, const sol_d
     return e == hipSuccess ? SOL_OK : SOL_ERR_HIP;
 }
 
+sol_status sol_qk_norm_rope_pool(const void* q, const void* k, const sol_desc* desc,
+                                 const float* gamma_q, const float* gamma_k, float eps,
+                                 const float* rope_cos, const float* rope_sin, int32_t sink_len,
+                                 void* q_out, void* k_out, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+    sol::Geom g;
+    const sol_status st = check_desc(desc, sink_len, &g);
+    if (st != SOL_OK) return st;
+    if (q == nullptr || k == nullptr || q_out == nullptr || k_out == nullptr ||
+        gamma_q == nullptr || gamma_k == nullptr || q_out == k_out || q_out == k || k_out == q)
+        return SOL_ERR_ARG;
+    if ((rope_cos == nullptr) != (rope_sin == nullptr)) return SOL_ERR_ARG;
+    if (!(eps >= 0.0f) || std::isinf(eps)) return SOL_ERR_ARG;
+    // in place only with identical input and output strides
+    const bool same_strides = desc->qkv_sb == desc->o_sb && desc->qkv_sn == desc->o_sn &&
+                              desc->qkv_sh == desc->o_sh;
+    if ((q_out == q || k_out == k) && !same_strides) return SOL_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) ||
+        !aligned16(gamma_q) || !aligned16(gamma_k) || !aligned16(rope_cos) || !aligned16(rope_sin))
+        return SOL_ERR_ALIGN;
+    const size_t need = sol::route_ws_floats(g) * sizeof(float);
+    if (workspace == nullptr || ws_bytes < need) return SOL_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SOL_ERR_ALIGN;
+    const hipError_t e = sol::launch_qk_norm_rope_pool(g, q, k, gamma_q, gamma_k, eps, rope_cos,
+                                                       rope_sin, q_out, k_out,
+                                                       static_cast<float*>(workspace),
+                                                       static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOL_OK : SOL_ERR_HIP;
+}
+
+sol_status sol_route_pooled(const sol_desc* desc, float tau, int32_t sink_len, float scale,
+                            int16_t* blk_idx, int32_t* blk_cnt, int64_t* totals, int32_t* order,
+                            const void* workspace, size_t ws_bytes, void* stream) {
+    sol::Geom g;
+    const sol_status st = check_desc(desc, sink_len, &g);
+    if (st != SOL_OK) return st;
+    if (blk_idx == nullptr || blk_cnt == nullptr || totals == nullptr) return SOL_ERR_ARG;
+    if (std::isnan(tau) || tau < 0.0f || std::isnan(scale) || scale < 0.0f || std::isinf(scale))
+        return SOL_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(totals) & 7u) != 0 ||
+        (reinterpret_cast<uintptr_t>(blk_cnt) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(blk_idx) & 1u) != 0 ||
+        (reinterpret_cast<uintptr_t>(order) & 3u) != 0)
+        return SOL_ERR_ALIGN;
+    if (g.NB > 32767 || g.ncand > kMaxCandidates) return SOL_ERR_UNSUPPORTED;
+    const size_t need = sol::route_ws_floats(g) * sizeof(float);
+    if (workspace == nullptr || ws_bytes < need) return SOL_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SOL_ERR_ALIGN;
+    const hipError_t e = sol::launch_route_pooled(g, resolve_scale(scale, g.D), tau, blk_idx, blk_cnt,
+                                                  totals, order,
+                                                  static_cast<const float*>(workspace),
+                                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOL_OK : SOL_ERR_HIP;
+}
+
 const char* sol_status_str(sol_status status) {
     switch (status) {
         case SOL_OK: return "ok";

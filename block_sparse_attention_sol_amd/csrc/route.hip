@@ -320,6 +320,11 @@ __global__ __launch_bounds__(256) void empty_route_kernel(int32_t* __restrict__ 
     }
 }
 
+// totals start at zero when routing starts from block means written elsewhere
+__global__ __launch_bounds__(64) void clear_totals_kernel(int64_t* __restrict__ totals) {
+    if (threadIdx.x < 2) totals[threadIdx.x] = 0;
+}
+
 // Attention schedule: the query blocks of each (batch, head) sorted by list
 // length, longest first (a counting sort over the lengths 0..ncand).  Running
 // the long walks first balances the tail of the attention launch, and query
@@ -396,6 +401,19 @@ hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, fl
     return hipGetLastError();
 }
 
+// scores and selection from the block means, then the schedule
+hipError_t select_and_order(const Geom& g, const float* qbar, const float* kbar, float scale,
+                            float tau, int16_t* idx, int32_t* cnt, int64_t* totals,
+                            int32_t* order, hipStream_t stream)
+{
+    hipError_t e = g.D == 128 ? launch_select<128>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream)
+                              : launch_select<64>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream);
+    if (e != hipSuccess || order == nullptr) return e;
+    hipLaunchKernelGGL(order_kernel, dim3(g.B * g.H), dim3(256), (size_t)(g.ncand + 1) * sizeof(int),
+                       stream, cnt, g, order);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t route_ws_floats(const Geom& g) {
@@ -421,14 +439,26 @@ hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale
     dim3 grid(g.NB, (lanes + 255) / 256, g.B * 2);
     hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, stream, (const uint16_t*)q,
                        (const uint16_t*)k, g, qbar, kbar, totals);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = g.D == 128 ? launch_select<128>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream)
-                   : launch_select<64>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream);
-    if (e != hipSuccess || order == nullptr) return e;
-    hipLaunchKernelGGL(order_kernel, dim3(g.B * g.H), dim3(256), (size_t)(g.ncand + 1) * sizeof(int),
-                       stream, cnt, g, order);
-    return hipGetLastError();
+    return select_and_order(g, qbar, kbar, scale, tau, idx, cnt, totals, order, stream);
+}
+
+hipError_t launch_route_pooled(const Geom& g, float scale, float tau, int16_t* idx, int32_t* cnt,
+                               int64_t* totals, int32_t* order, const float* ws,
+                               hipStream_t stream)
+{
+    if (g.ncand == 0) {
+        const int n = g.B * g.H * g.NB;
+        hipLaunchKernelGGL(empty_route_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cnt, g,
+                           totals, order);
+        return hipGetLastError();
+    }
+    const size_t one = ((size_t)g.B * g.H * g.NB * g.D + 63) / 64 * 64;
+    hipLaunchKernelGGL(clear_totals_kernel, dim3(1), dim3(64), 0, stream, totals);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return select_and_order(g, ws, ws + one, scale, tau, idx, cnt, totals, order, stream);
 }
 
 }  // namespace sol

@@ -76,6 +76,18 @@ hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale
                         hipStream_t stream);
 size_t route_ws_floats(const Geom& g);
 
+// Routing from block means already in ws (written by launch_qk_norm_rope_pool).
+hipError_t launch_route_pooled(const Geom& g, float scale, float tau, int16_t* idx, int32_t* cnt,
+                               int64_t* totals, int32_t* order, const float* ws,
+                               hipStream_t stream);
+
+// QK-norm + RoPE producer that also writes the block means into ws (the
+// routing workspace layout).  rope_cos / rope_sin may both be null (no RoPE).
+hipError_t launch_qk_norm_rope_pool(const Geom& g, const void* q, const void* k,
+                                    const float* gamma_q, const float* gamma_k, float eps,
+                                    const float* rope_cos, const float* rope_sin, void* q_out,
+                                    void* k_out, float* ws, hipStream_t stream);
+
 // Attention launches; order (nullable) is the routing schedule.
 hipError_t launch_attn(const Geom& g, const void* q, const void* k, const void* v,
                        const int16_t* idx, const int32_t* cnt, const int32_t* order, float scale,

@@ -52,6 +52,10 @@ def _load():
     lib.sol_attn_dense_fwd.restype = ctypes.c_int
     lib.sol_gate_fwd.argtypes = [vp, vp, vp, dp, vp, vp, vp, i32, f32, vp, vp, vp, vp]
     lib.sol_gate_fwd.restype = ctypes.c_int
+    lib.sol_qk_norm_rope_pool.argtypes = [vp, vp, dp, vp, vp, f32, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.sol_qk_norm_rope_pool.restype = ctypes.c_int
+    lib.sol_route_pooled.argtypes = [dp, f32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
+    lib.sol_route_pooled.restype = ctypes.c_int
     lib.sol_status_str.argtypes, lib.sol_status_str.restype = [ctypes.c_int], ctypes.c_char_p
     _ = i64
     return lib
@@ -251,6 +255,58 @@ def forward(q, k, v, tau: float, sink: int, scale: float = 0.0, return_lse=False
     if return_lse:
         return res[0], res[1], idx, cnt, totals
     return res, idx, cnt, totals
+
+
+def qk_norm_rope_pool(q, k, gamma_q, gamma_k, eps: float, rope_cos=None, rope_sin=None,
+                      sink: int = 0, out=None, workspace=None, cu_seqlens=None, max_seqlen=None):
+    """QK-norm + RoPE of q and k into bf16 outputs, with the block means of the outputs
+    written into the routing workspace.  Returns (q_out, k_out, workspace); pass the
+    workspace to route_pooled().  ``out`` = (q_out, k_out) may be (q, k) (in place).
+    gamma_* are float32 [D]; rope_cos / rope_sin float32 [N, D/2] or None."""
+    _check_qkv(q, k)
+    desc = make_desc(q, None if out is None else out[0], cu_seqlens, max_seqlen)
+    q_out, k_out = (torch.empty_like(q), torch.empty_like(k)) if out is None else out
+    for t in (q_out, k_out):
+        if (not t.is_cuda or t.dtype != torch.bfloat16 or t.shape != q.shape
+                or t.stride() != q_out.stride()):
+            raise ValueError("q_out and k_out must be bf16 with q's shape and one set of strides")
+    for t in (gamma_q, gamma_k, rope_cos, rope_sin):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()
+                              or t.device != q.device):
+            raise ValueError("gamma and RoPE tables must be contiguous float32 on q's device")
+    D = q.shape[-1]
+    if gamma_q.numel() != D or gamma_k.numel() != D:
+        raise ValueError("gamma_q and gamma_k need D entries")
+    if rope_cos is not None and (rope_sin is None or rope_cos.shape != rope_sin.shape
+                                 or rope_cos.dim() != 2 or rope_cos.shape[1] != D // 2
+                                 or rope_cos.shape[0] < desc.N):
+        raise ValueError("rope_cos and rope_sin must both be float32 [>= N, D/2]")
+    need = int(lib.sol_route_workspace_bytes(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.sol_qk_norm_rope_pool(q.data_ptr(), k.data_ptr(), ctypes.byref(desc),
+                                   gamma_q.data_ptr(), gamma_k.data_ptr(), ctypes.c_float(eps),
+                                   rope_cos.data_ptr() if rope_cos is not None else None,
+                                   rope_sin.data_ptr() if rope_sin is not None else None,
+                                   int(sink), q_out.data_ptr(), k_out.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel(), _stream(q))
+    _check(st, "sol_qk_norm_rope_pool")
+    return q_out, k_out, workspace
+
+
+def route_pooled(q, workspace, tau: float, sink: int, scale: float = 0.0, out=None,
+                 cu_seqlens=None, max_seqlen=None):
+    """Routing from the block means that qk_norm_rope_pool() left in ``workspace``
+    (q gives the shape only; its data is not read).  Same returns as route()."""
+    desc = make_desc(q, None, cu_seqlens, max_seqlen)
+    idx, cnt, totals, order = (route_outputs(q, cu_seqlens, max_seqlen) if out is None
+                               else out)
+    st = lib.sol_route_pooled(ctypes.byref(desc), ctypes.c_float(tau), int(sink),
+                              ctypes.c_float(scale), idx.data_ptr(), cnt.data_ptr(),
+                              totals.data_ptr(), order.data_ptr() if order is not None else None,
+                              workspace.data_ptr(), workspace.numel(), _stream(q))
+    _check(st, "sol_route_pooled")
+    return idx, cnt, totals, order
 
 
 def default_scale(D: int) -> float:

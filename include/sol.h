@@ -202,6 +202,60 @@ sol_status sol_gate_fwd(const void* q, const void* k, const void* v, const sol_d
                         int32_t sink_len, float scale, void* o_sparse, void* o_dense,
                         double* stats, void* stream);
 
+/*
+ * sol_qk_norm_rope_pool -- the producer right before the path: QK-norm and
+ * RoPE of the query and key rows, written as the bf16 Q and K that routing
+ * and attention read, and in the same pass the block means that routing
+ * scores (tokenfactory.fast post, "Custom kernels": a fused QK-norm plus
+ * RoPE kernel; clawpit.io article, paragraph on the Sol-Attn settings:
+ * routing from compressed queries and keys).  With it, routing never reads
+ * Q and K again: sol_route_pooled starts from the means.  The pages define
+ * neither operation; the plainest reading is taken and fixed in float32:
+ *
+ *   For every valid row x (one head, D channels) at position t of its
+ *   sample, with weights gamma (gamma_q for Q, gamma_k for K):
+ *     p_c  = fma chain over d = 8c .. 8c+7 ascending of x_d * x_d, from +0
+ *            (c = 0 .. D/8 - 1)
+ *     ss   = the balanced binary tree of the p_c in index order:
+ *            ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)) + ...
+ *     r    = 1 / sqrt(fma(ss, 1/D, eps))   (each step correctly rounded)
+ *     y_d  = (x_d * r) * gamma_d            (per-head RMS normalisation)
+ *     RoPE on the channel pairs (2i, 2i+1), with c = cos[t][i], s = sin[t][i]:
+ *       o_2i   = fma(y_2i, c, -(y_2i+1 * s))
+ *       o_2i+1 = fma(y_2i, s,   y_2i+1 * c)
+ *     out  = o rounded to bf16 (nearest even)
+ *   Block means, float32, of the rounded outputs: exactly the pooling of
+ *   sol_route applied to q_out and k_out (rows added in ascending order from
+ *   +0, one divide; key means over R(j) only), written into workspace.
+ *
+ *   q, k         in, [B, N, H, D] bf16 (Q/K/V strides of desc), or packed.
+ *   q_out, k_out out, bf16 with the O strides of desc; may equal q and k
+ *                (in place) when the O strides equal the Q/K/V strides.
+ *   gamma_q/_k   device float32 [D], 16-byte aligned.
+ *   eps          >= 0, finite.
+ *   rope_cos/sin device float32 [N, D/2] (row t = position t of a sample),
+ *                16-byte aligned; both NULL: no RoPE (o = y).
+ *   sink_len     S, for the key means over R(j).
+ *   workspace    as for sol_route (sol_route_workspace_bytes(desc) bytes,
+ *                256-byte aligned): receives the block means.
+ */
+sol_status sol_qk_norm_rope_pool(const void* q, const void* k, const sol_desc* desc,
+                                 const float* gamma_q, const float* gamma_k, float eps,
+                                 const float* rope_cos, const float* rope_sin, int32_t sink_len,
+                                 void* q_out, void* k_out, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/*
+ * sol_route_pooled -- sol_route from block means already in the workspace
+ * (written by sol_qk_norm_rope_pool for the same desc and sink_len): scores,
+ * selection, lists, totals and schedule exactly as sol_route computes them
+ * on q_out and k_out, without reading Q or K.  Arguments and errors as for
+ * sol_route.
+ */
+sol_status sol_route_pooled(const sol_desc* desc, float tau, int32_t sink_len, float scale,
+                            int16_t* blk_idx, int32_t* blk_cnt, int64_t* totals, int32_t* order,
+                            const void* workspace, size_t ws_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* sol_status_str(sol_status status);
 

@@ -4,7 +4,7 @@ Test infrastructure: prints, for each workload, the tau (4 significant digits)
 whose routed density is nearest the target, and the exact density it gives.
 The frozen values live in synth.WORKLOADS.  Calls only oracle/ and synth/.
 
-    python -m oracle.calibrate_tau [tiny mid page varlen]
+    python -m oracle.calibrate_tau [tiny mid page page_fused varlen]
 """
 
 from __future__ import annotations
@@ -17,11 +17,16 @@ import numpy as np
 import synth
 from oracle import oracle as orc
 
-TARGET = {"tiny": 0.25, "mid": 0.20, "page": 0.19}
+TARGET = {"tiny": 0.25, "mid": 0.20, "page": 0.19, "page_fused": 0.19}
 
 
 def scores_for(w: synth.Workload):
     q, k, _ = synth.make_qkv(w)
+    if w.producer:
+        gq, gk = synth.norm_weights(w.D)
+        cos, sin = synth.rope_tables(w.N, w.D)
+        q = orc.qk_norm_rope(q, gq, synth.NORM_EPS, cos, sin)
+        k = orc.qk_norm_rope(k, gk, synth.NORM_EPS, cos, sin)
     q32, k32 = synth.bf16_bits_to_f32(q), synth.bf16_bits_to_f32(k)
     g = orc.geometry(w.N, w.sink)
     s = orc.block_scores(orc.pool_queries(q32, g), orc.pool_keys(k32, g), g,

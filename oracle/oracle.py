@@ -74,6 +74,10 @@ def _clib():
         lib.oracle_block_scores.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                             ctypes.c_void_p]
+        lib.oracle_qk_norm_rope.restype = None
+        lib.oracle_qk_norm_rope.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -401,3 +405,59 @@ def attention_packed(q: np.ndarray, k: np.ndarray, v: np.ndarray, routes, cu,
         O[cu[b]:cu[b + 1]] = o[0]
         Ls.append(lse[0])
     return O, Ls
+
+
+# --------------------------------------------------------------------------- producer
+# QK-norm plus RoPE, the op the tokenfactory.fast post ("Custom kernels") fuses
+# right before attention.  The pages define neither part; the reading taken:
+# per-head RMS normalisation over the D channels with a weight per channel and
+# a small eps, then RoPE rotating channel pairs (2i, 2i + 1) by the angle whose
+# cosine and sine tables give for the row's position in its sample.  Routing
+# then pools the producer's bf16 outputs exactly as it pools Q and K.
+
+def qk_norm_rope_f64(x: np.ndarray, gamma: np.ndarray, eps: float, cos=None, sin=None):
+    """The definition in float64, no rounding: x [..., N, H, D] (any float), cos/sin
+    [N, D/2] for the row positions (or None).  Returns float64 of x's shape."""
+    x = np.asarray(x, np.float64)
+    ms = (x * x).mean(axis=-1, keepdims=True)
+    y = x / np.sqrt(ms + float(eps)) * np.asarray(gamma, np.float64)
+    if cos is None:
+        return y
+    c = np.asarray(cos, np.float64)[:, None, :]           # [N, 1, D/2], broadcast over heads
+    s = np.asarray(sin, np.float64)[:, None, :]
+    a, b = y[..., 0::2], y[..., 1::2]
+    out = np.empty_like(y)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = a * s + b * c
+    return out
+
+
+def qk_norm_rope(x_bits: np.ndarray, gamma: np.ndarray, eps: float, cos=None, sin=None):
+    """The float32 mirror (score_ref.c): [B, N, H, D] bf16 bits -> bf16 bits."""
+    B, N, H, D = x_bits.shape
+    lib = _clib()
+    g = np.ascontiguousarray(gamma, np.float32)
+    cs = None if cos is None else np.ascontiguousarray(cos[:N], np.float32)
+    sn = None if sin is None else np.ascontiguousarray(sin[:N], np.float32)
+    out = np.empty_like(x_bits)
+    for b in range(B):
+        for h in range(H):
+            xi = np.ascontiguousarray(x_bits[b, :, h, :], np.uint16)
+            oi = np.empty_like(xi)
+            lib.oracle_qk_norm_rope(xi.ctypes.data, N, D, g.ctypes.data, ctypes.c_float(eps),
+                                    None if cs is None else cs.ctypes.data,
+                                    None if sn is None else sn.ctypes.data, oi.ctypes.data)
+            out[b, :, h, :] = oi
+    return out
+
+
+def qk_norm_rope_packed(x_bits: np.ndarray, cu, gamma, eps: float, cos=None, sin=None):
+    """The mirror on a packed [T, H, D] batch: positions restart at 0 in every sample;
+    rows outside the samples are returned unchanged."""
+    out = x_bits.copy()
+    cu = [int(c) for c in cu]
+    for b in range(len(cu) - 1):
+        if cu[b + 1] > cu[b]:
+            out[cu[b]:cu[b + 1]] = qk_norm_rope(x_bits[None, cu[b]:cu[b + 1]], gamma, eps,
+                                                cos, sin)[0]
+    return out

@@ -1,6 +1,7 @@
 /*
- * CPU oracle, pooled block scores.  TEST INFRASTRUCTURE ONLY: nothing on the
- * product path links or calls this file.
+ * CPU oracle, float32 mirrors: pooled block scores, and the QK-norm + RoPE
+ * producer (second half of this file).  TEST INFRASTRUCTURE ONLY: nothing on
+ * the product path links or calls this file.
  *
  * Online routing in Sol-Attn compares compressed (block-pooled) queries with
  * compressed keys, per head (clawpit.io article on the single-4090 run,
@@ -18,6 +19,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 void oracle_block_scores(const float *qbar, const float *kbar, int64_t nq, int64_t nk,
                          int64_t d, float scale, float *out)
@@ -31,5 +33,75 @@ void oracle_block_scores(const float *qbar, const float *kbar, int64_t nq, int64
                 acc = fmaf(qi[t], kj[t], acc);
             out[i * nk + j] = acc * scale;
         }
+    }
+}
+
+/*
+ * QK-norm + RoPE, float32 mirror.  QK-norm plus RoPE is the fused op the
+ * tokenfactory.fast post ("Custom kernels") names right before attention; the
+ * pages define neither, so the reading is per-head RMS normalisation with a
+ * weight per channel, then the rotation of channel pairs (2i, 2i + 1) by the
+ * angle whose cosine and sine the caller tables give for the row's position.
+ * One row x of D bf16 values, written step by step in one fixed float32 order:
+ *
+ *   p[c]  = fmaf chain over the 8 channels 8c .. 8c+7 ascending of x*x, from +0
+ *   ss    = balanced binary tree of p[0 .. D/8-1] in index order
+ *   r     = 1 / sqrtf(fmaf(ss, 1/D, eps))
+ *   y[d]  = (x[d] * r) * gamma[d]
+ *   o[2i] = fmaf(y[2i], c, -(y[2i+1] * s)),  o[2i+1] = fmaf(y[2i], s, y[2i+1] * c)
+ *   out   = o rounded to bf16, nearest even
+ *
+ * x and out are rows x d bf16 bit patterns; cosv / sinv are rows x d/2 (the
+ * row's position already applied) or both NULL for no rotation.
+ */
+static float bf16_to_f32(uint16_t b)
+{
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+void oracle_qk_norm_rope(const uint16_t *x, int64_t rows, int64_t d, const float *gamma,
+                         float eps, const float *cosv, const float *sinv, uint16_t *out)
+{
+    const int64_t nch = d / 8;
+    for (int64_t t = 0; t < rows; ++t) {
+        const uint16_t *xr = x + t * d;
+        float p[64];
+        for (int64_t c = 0; c < nch; ++c) {
+            float acc = 0.0f;
+            for (int64_t e = 0; e < 8; ++e) {
+                const float v = bf16_to_f32(xr[8 * c + e]);
+                acc = fmaf(v, v, acc);
+            }
+            p[c] = acc;
+        }
+        for (int64_t w = 1; w < nch; w *= 2)
+            for (int64_t c = 0; c + w < nch; c += 2 * w)
+                p[c] = p[c] + p[c + w];
+        const float r = 1.0f / sqrtf(fmaf(p[0], 1.0f / (float)d, eps));
+        float y[512];
+        for (int64_t e = 0; e < d; ++e)
+            y[e] = (bf16_to_f32(xr[e]) * r) * gamma[e];
+        if (cosv != NULL) {
+            for (int64_t i = 0; i < d / 2; ++i) {
+                const float c = cosv[t * (d / 2) + i], s = sinv[t * (d / 2) + i];
+                const float a = y[2 * i], b = y[2 * i + 1];
+                y[2 * i] = fmaf(a, c, -(b * s));
+                y[2 * i + 1] = fmaf(a, s, b * c);
+            }
+        }
+        for (int64_t e = 0; e < d; ++e)
+            out[t * d + e] = f32_to_bf16_rne(y[e]);
     }
 }

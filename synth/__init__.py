@@ -80,6 +80,7 @@ class Workload:
     beta: float = 0.0  # spatial-basis amplitude (field only)
     seed: int = 0
     dense: bool = False  # routing disabled (full attention)
+    producer: bool = False  # Q, K pass through QK-norm + RoPE before routing (norm_weights, rope_tables)
 
     @property
     def n_blocks(self) -> int:
@@ -93,6 +94,9 @@ class Workload:
 # tau values were calibrated on the oracle's routing so that the routed
 # density lands near the stated target; ``oracle/calibrate_tau.py`` recomputes
 # them and prints the exact densities they give.
+# eps of the synthetic QK-norm (a model hyperparameter; 1e-6 is common)
+NORM_EPS = 1e-6
+
 WORKLOADS = {
     # ~25% routed density
     "tiny": Workload("tiny", B=1, N=1024, H=4, D=64, sink=64, tau=0.5019, kind="tiny"),
@@ -106,6 +110,10 @@ WORKLOADS = {
     "page_dense": Workload("page_dense", B=1, N=38247, H=56, D=128, sink=951,
                            tau=math.inf, kind="field", frames=124, alpha=1.0, beta=1.0,
                            dense=True),
+    # the pages' shape with the QK-norm + RoPE producer in front of routing
+    # (the same raw tensors as "page"; tau recalibrated on the producer's outputs)
+    "page_fused": Workload("page_fused", B=1, N=38247, H=56, D=128, sink=951, tau=0.7832,
+                           kind="field", frames=124, alpha=1.0, beta=1.0, producer=True),
     # one GPU's share of a 4-way head split; N varies per call (see varlen_calls)
     "varlen": Workload("varlen", B=1, N=38000, H=14, D=128, sink=951, tau=1.951,
                        kind="field", frames=124, alpha=1.0, beta=1.0),
@@ -232,3 +240,19 @@ def packed_batch(calls: list[Workload], threads: int = 8):
             out[t][s0:s1] = x[0]
     return out[0], out[1], out[2], cu
 
+
+
+def norm_weights(D: int, seed: int = 0):
+    """Synthetic QK-norm weights (gamma_q, gamma_k), float32 [D] each: 1 + 0.1 N(0, 1)."""
+    rng = np.random.default_rng([seed, 0x9A])
+    return (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32), \
+        (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+
+
+def rope_tables(N: int, D: int, base: float = 10000.0):
+    """Cosine and sine tables float32 [N, D/2] of rotary positions 0 .. N-1: pair i of
+    position t turns by t * base^(-2i/D) (computed in float64, rounded once)."""
+    t = np.arange(N, dtype=np.float64)[:, None]
+    inv = base ** (-np.arange(0, D, 2, dtype=np.float64) / D)[None, :]
+    ang = t * inv
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)

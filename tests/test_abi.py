@@ -216,3 +216,80 @@ def test_gate_argument_errors(lib):
     assert gate(sink=-1) == 1
     d = _packed_desc(lib, osb=1024)
     assert gate() == 1                      # a packed batch takes no output batch stride
+
+
+def _producer(lib, desc, q=0x10000, k=0x20000, gq=0x30000, gk=0x31000, eps=1e-6, cos=0x40000,
+              sin=0x50000, sink=64, qo=0x60000, ko=0x70000, ws=0x80000, ws_bytes=1 << 40):
+    return lib.lib.sol_qk_norm_rope_pool(q, k, ctypes.byref(desc), gq, gk, ctypes.c_float(eps),
+                                         cos, sin, sink, qo, ko, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_gamma", 1), ("one_rope_table", 1), ("nan_eps", 1), ("negative_eps", 1),
+    ("inf_eps", 1), ("same_outputs", 1), ("q_out_is_k", 1), ("in_place_other_strides", 1),
+    ("misaligned_gamma", 3), ("misaligned_cos", 3), ("misaligned_out", 3), ("small_workspace", 4),
+    ("D96", 2), ("negative_sink", 1),
+])
+def test_producer_argument_errors(lib, case, expect):
+    d = _desc(lib)
+    kw = {}
+    if case == "null_gamma":
+        kw["gk"] = None
+    elif case == "one_rope_table":
+        kw["sin"] = None
+    elif case == "nan_eps":
+        kw["eps"] = math.nan
+    elif case == "negative_eps":
+        kw["eps"] = -1e-6
+    elif case == "inf_eps":
+        kw["eps"] = math.inf
+    elif case == "same_outputs":
+        kw["ko"] = 0x60000
+    elif case == "q_out_is_k":
+        kw["qo"] = 0x20000
+    elif case == "in_place_other_strides":
+        d = lib.Desc(1, 1000, 2, 128, 256000, 256, 128, 512000, 512, 128)
+        kw["qo"] = 0x10000
+    elif case == "misaligned_gamma":
+        kw["gq"] = 0x30004
+    elif case == "misaligned_cos":
+        kw["cos"] = 0x40008
+    elif case == "misaligned_out":
+        kw["ko"] = 0x70002
+    elif case == "small_workspace":
+        kw["ws_bytes"] = 64
+    elif case == "D96":
+        d = _desc(lib, D=96)
+    elif case == "negative_sink":
+        kw["sink"] = -3
+    assert _producer(lib, d, **kw) == expect
+
+
+def test_producer_in_place_with_equal_strides_passes_the_checks(lib):
+    # equal strides make in place legal; a null workspace is then the first
+    # (and only) rule broken, so nothing reaches the device
+    d = _desc(lib)
+    assert _producer(lib, d, qo=0x10000, ko=0x20000, ws=None) == 4
+
+
+def test_route_pooled_argument_errors(lib):
+    d = _desc(lib)
+
+    def rp(**kw):
+        a = dict(tau=1.0, sink=64, scale=0.0, idx=0x30000, cnt=0x40000, tot=0x50000, order=None,
+                 ws=0x60000, ws_bytes=1 << 40, desc=d)
+        a.update(kw)
+        return lib.lib.sol_route_pooled(ctypes.byref(a["desc"]), ctypes.c_float(a["tau"]),
+                                        a["sink"], ctypes.c_float(a["scale"]), a["idx"], a["cnt"],
+                                        a["tot"], a["order"], a["ws"], a["ws_bytes"], None)
+    assert rp(tau=math.nan) == 1
+    assert rp(tau=-1.0) == 1
+    assert rp(idx=None) == 1
+    assert rp(tot=0x50004) == 3
+    assert rp(order=0x70002) == 3
+    assert rp(ws=None) == 4
+    assert rp(ws_bytes=8) == 4
+    assert rp(ws=0x60040) == 3
+    assert rp(desc=_desc(lib, N=64 * 5000, H=1)) == 2
+    assert lib.lib.sol_route_pooled(None, ctypes.c_float(1.0), 0, ctypes.c_float(0.0), 0x30000,
+                                    0x40000, 0x50000, None, 0x60000, 1 << 30, None) == 1
