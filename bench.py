@@ -139,9 +139,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="page",
-                    choices=["page", "page_dense", "mid", "varlen_packed"],
+                    choices=["page", "page_dense", "mid", "varlen_packed", "page_fused"],
                     help="varlen_packed: the 16 variable-length prompts (N in [36000, 40000], "
-                         "H = 14) packed into one call")
+                         "H = 14) packed into one call; page_fused: the pages' shape with the "
+                         "QK-norm + RoPE producer in front, routing from its block means")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2048)
     ap.add_argument("--cpu-heads", type=int, default=4)
@@ -211,20 +212,40 @@ def main() -> int:
     ws = torch.empty(max(sol.route_workspace_bytes(q, **vk), 256), dtype=torch.uint8, device=dev)
     outs = sol.route_outputs(q, **vk)
     idx, cnt, totals, order = outs
+    producer = w.producer
+    qa, ka = q, k                      # what attention reads
+    if producer:
+        # raw projections in q, k; the producer writes normalised, rotated qa, ka
+        gq, gk = synth.norm_weights(D)
+        cos, sin = synth.rope_tables(N, D)
+        pargs = tuple(torch.from_numpy(x).to(dev) for x in (gq, gk)) + (synth.NORM_EPS,) + \
+            tuple(torch.from_numpy(x).to(dev) for x in (cos, sin))
+        qa, ka = torch.empty_like(q), torch.empty_like(k)
+
+    def routing_stage(mark=None):
+        if producer:
+            sol.qk_norm_rope_pool(q, k, *pargs, sink=w.sink, out=(qa, ka), workspace=ws, **vk)
+            if mark is not None:
+                mark.record()
+            sol.route_pooled(q, ws, w.tau, w.sink, out=outs, **vk)
+        else:
+            if mark is not None:
+                mark.record()
+            sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs, **vk)
 
     def step():
         if dense:
             sol.attn_dense(q, k, v, out=o, **vk)
         else:
-            sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs, **vk)
-            sol.attn(q, k, v, idx, cnt, w.sink, out=o, order=order, **vk)
+            routing_stage()
+            sol.attn(qa, ka, v, idx, cnt, w.sink, out=o, order=order, **vk)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # per-kernel events on the stream the kernels run on (torch's current stream)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -232,19 +253,23 @@ def main() -> int:
     for s in range(args.steps):
         ev[s][0].record()
         if not dense:
-            sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs, **vk)
-        ev[s][1].record()
+            routing_stage(ev[s][1])
+        else:
+            ev[s][1].record()
+        ev[s][2].record()
         if dense:
             sol.attn_dense(q, k, v, out=o, **vk)
         else:
-            sol.attn(q, k, v, idx, cnt, w.sink, out=o, order=order, **vk)
-        ev[s][2].record()
+            sol.attn(qa, ka, v, idx, cnt, w.sink, out=o, order=order, **vk)
+        ev[s][3].record()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(end) / args.steps
-    route_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    prod_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    route_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    attn_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    t_prod = float(np.mean(prod_ms)) if producer else 0.0
     t_route = float(np.mean(route_ms)) if not dense else 0.0
     t_attn = float(np.mean(attn_ms))
     sep_ms = None
@@ -287,12 +312,21 @@ def main() -> int:
     tflops = flop_eff / (ms_step * 1e-3) / 1e12
     attn_tflops = flop_eff / (t_attn * 1e-3) / 1e12
     route_bytes = (sum(n * H * D * 2 + max(n - w.sink, 0) * H * D * 2 for n in lengths)
-                   + 2 * routed + 4 * B * H * NB + 16) if not dense else 0
-    route_gbs = route_bytes / (t_route * 1e-3) / 1e9 if not dense else None
+                   + 2 * routed + 4 * B * H * NB + 16) if not (dense or producer) else 0
+    route_gbs = route_bytes / (t_route * 1e-3) / 1e9 if route_bytes else None
+    prod_gbs = None
+    if producer:
+        # Q and K read and written once, the block means written, tables and weights read
+        prod_bytes = (4 * sum(lengths) * H * D * 2 + 2 * B * H * NB * D * 4 + 2 * N * (D // 2) * 4
+                      + 2 * D * 4)
+        prod_gbs = prod_bytes / (t_prod * 1e-3) / 1e9
+        err(f"producer (QK-norm + RoPE + block means): {t_prod:.3f} ms, {prod_gbs:.0f} GB/s "
+            f"({prod_gbs / PEAK_HBM_GBS:.1%} of HBM peak)")
     err(f"{args.workload}: {ms_step:.3f} ms/forward (route {t_route:.3f} ms, attention {t_attn:.3f} ms), "
         f"effective {tflops:.1f} TFLOP/s, attention {attn_tflops:.1f} TFLOP/s "
         f"({attn_tflops / PEAK_BF16_TFLOPS:.1%} of bf16 peak), routing "
-        f"{(route_gbs or 0):.0f} GB/s; route density {rho_route:.4%}, pair density {rho_pair:.4%}; "
+        f"{f'{route_gbs:.0f} GB/s' if route_gbs else 'from block means'}; "
+        f"route density {rho_route:.4%}, pair density {rho_pair:.4%}; "
         f"wall {wall:.2f} s for {args.steps} steps")
 
     # the committed counter runs cover the pages' sparse shape only
@@ -304,6 +338,10 @@ def main() -> int:
                 f"blocks, tau {w.tau}")
     elif dense:
         desc = f"{w.name}: dense attention (routing disabled) on [{B},{N},{H},{D}] bf16"
+    elif producer:
+        desc = (f"{w.name}: QK-norm + RoPE producer writing Q, K and their block means, routing "
+                f"from the means, then sink/routed attention on [{B},{N},{H},{D}] bf16, sink "
+                f"{w.sink}, 64-token blocks, tau {w.tau}")
     else:
         desc = (f"{w.name}: one Sol-Attn forward (routing + sink/routed attention) on "
                 f"[{B},{N},{H},{D}] bf16, sink {w.sink}, 64-token blocks, tau {w.tau}")
@@ -326,6 +364,8 @@ def main() -> int:
             "route_density": round(rho_route, 6), "pair_density": round(rho_pair, 6),
             "routed_block_pairs": routed, "attended_pairs": pairs,
             "route_ms": round(t_route, 4), "attn_ms": round(t_attn, 4),
+            **({"producer_ms": round(t_prod, 4), "producer_gbs": round(prod_gbs, 1),
+                "producer_hbm_frac": round(prod_gbs / PEAK_HBM_GBS, 4)} if producer else {}),
             "route_gbs": round(route_gbs, 1) if route_gbs else None,
             "route_hbm_frac": round(route_gbs / PEAK_HBM_GBS, 4) if route_gbs else None,
         },
@@ -338,9 +378,9 @@ def main() -> int:
             "traffic": traffic,
         },
     }
-    if packed and not args.no_cpu_baseline:
+    if (packed or producer) and not args.no_cpu_baseline:
         err("cpu baseline: timed on the default (pages' shape) workload only")
-    if not args.no_cpu_baseline and not packed:
+    if not args.no_cpu_baseline and not packed and not producer:
         t0 = time.perf_counter()
         rec["cpu_baseline"] = cpu_baseline(w, q_bits, k_bits, v_bits, args.cpu_heads, args.cpu_blocks,
                                            flop_eff)
