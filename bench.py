@@ -8,7 +8,14 @@ prefix sink plus the routed 64-token key blocks) at the pages' shape
 HBM before the timed region.  Prints one JSON line on stdout; diagnostics go
 to stderr.
 
+The K timed steps run back to back (the headline value).  Then K more
+forwards each follow a 512 MiB scratch write that evicts L2 and the MALL, and
+both sets are reported as median, p10 and p90 per forward.  Other workloads:
+page_dense, mid, varlen_packed (16 prompts in one packed call) and page_fused
+(QK-norm + RoPE producer, routing from its block means, attention).
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--workload page|page_dense|mid|varlen_packed|page_fused]
 """
 
 from __future__ import annotations
@@ -272,6 +279,25 @@ def main() -> int:
     t_prod = float(np.mean(prod_ms)) if producer else 0.0
     t_route = float(np.mean(route_ms)) if not dense else 0.0
     t_attn = float(np.mean(attn_ms))
+    step_ms = [e[0].elapsed_time(e[3]) for e in ev]
+
+    # cold-cache repetitions: a 512 MiB scratch write before each forward
+    # evicts L2 and the MALL; only the forward itself is timed
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_ms = []
+    for _ in range(args.steps):
+        scratch.fill_(1)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        step()
+        c1.record()
+        torch.cuda.synchronize()
+        cold_ms.append(c0.elapsed_time(c1))
+    del scratch
+
+    def spread(x):
+        return {"median": round(float(np.median(x)), 4), "p10": round(float(np.percentile(x, 10)), 4),
+                "p90": round(float(np.percentile(x, 90)), 4)}
     sep_ms = None
     if packed:
         # the same prompts as one fixed-length call each, for comparison
@@ -329,6 +355,10 @@ def main() -> int:
         f"route density {rho_route:.4%}, pair density {rho_pair:.4%}; "
         f"wall {wall:.2f} s for {args.steps} steps")
 
+    err(f"per forward: warm median {np.median(step_ms):.3f} ms (p10 {np.percentile(step_ms, 10):.3f}, "
+        f"p90 {np.percentile(step_ms, 90):.3f}); cold (L2 and MALL evicted) median "
+        f"{np.median(cold_ms):.3f} ms (p10 {np.percentile(cold_ms, 10):.3f}, "
+        f"p90 {np.percentile(cold_ms, 90):.3f})")
     # the committed counter runs cover the pages' sparse shape only
     traffic = measured_traffic() if args.workload == "page" else None
     if packed:
@@ -364,6 +394,7 @@ def main() -> int:
             "route_density": round(rho_route, 6), "pair_density": round(rho_pair, 6),
             "routed_block_pairs": routed, "attended_pairs": pairs,
             "route_ms": round(t_route, 4), "attn_ms": round(t_attn, 4),
+            "warm_ms_per_forward": spread(step_ms), "cold_ms_per_forward": spread(cold_ms),
             **({"producer_ms": round(t_prod, 4), "producer_gbs": round(prod_gbs, 1),
                 "producer_hbm_frac": round(prod_gbs / PEAK_HBM_GBS, 4)} if producer else {}),
             "route_gbs": round(route_gbs, 1) if route_gbs else None,
