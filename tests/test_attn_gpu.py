@@ -30,11 +30,12 @@ def sol():
     return s
 
 
-def _run(sol, w: synth.Workload, blocks=None, dense=False, tau=None):
-    """GPU route + attention on workload w, compared with the oracle on `blocks` (or all)."""
+def _run(sol, w: synth.Workload, blocks=None, dense=False, tau=None, inputs=None):
+    """GPU route + attention on workload w, compared with the oracle on `blocks` (or all).
+    ``inputs`` are w's (q, k, v) bits when the caller already drew them."""
     import torch
     tau = w.tau if tau is None else tau
-    q_bits, k_bits, v_bits = synth.make_qkv(w)
+    q_bits, k_bits, v_bits = synth.make_qkv(w) if inputs is None else inputs
     q32, k32, v32 = (synth.bf16_bits_to_f32(x) for x in (q_bits, k_bits, v_bits))
     q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
     if dense:
@@ -127,6 +128,26 @@ def test_attention_parity_edge_shapes(sol, B, N, H, D, S, tau):
     w = synth.Workload("edge", B=B, N=N, H=H, D=D, sink=S, tau=tau, kind="field", alpha=1.0,
                        seed=N + S)
     _run(sol, w)
+
+
+@pytest.fixture(scope="module")
+def maxcand_inputs():
+    w = synth.Workload("maxcand", B=1, N=263000, H=1, D=128, sink=951, tau=1.0, kind="field",
+                       alpha=1.0, seed=11)
+    return w, synth.make_qkv(w)
+
+
+@pytest.mark.parametrize("tau", [math.inf, 0.5])
+def test_maximum_candidates(sol, maxcand_inputs, tau):
+    """The largest routing problem the library accepts: 4096 candidate key
+    blocks per query block (N = 263000 with the 951-token sink, a ragged tail
+    of 24 rows).  At tau = inf every list holds all 4096 candidates, the most
+    a walk can take; routing is compared bit for bit and attention on sampled
+    blocks (first, straddle, last included)."""
+    w, inputs = maxcand_inputs
+    g = orc.geometry(w.N, w.sink)
+    assert g.ncand == 4096
+    _run(sol, w, blocks=sample_blocks(g, 1, 1, 12, seed=5), tau=tau, inputs=inputs)
 
 
 @pytest.mark.parametrize("N,D", [(1, 64), (200, 128), (1000, 64), (3001, 128)])
