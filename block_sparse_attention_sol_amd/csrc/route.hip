@@ -383,7 +383,9 @@ hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, fl
                          hipStream_t stream)
 {
     // candidates per lane: up to 4, so each q-bar value read from LDS feeds
-    // up to 4 FMAs; 16 waves x 64 lanes x 4 cover the 4096-candidate limit
+    // up to 4 FMAs; 16 waves x 64 lanes x 4 cover the 4096-candidate limit.
+    // Query blocks per workgroup: 12 with 4 candidates per lane (each k-bar
+    // chunk a lane loads then feeds 12 x 8 x 4 FMAs), 16 otherwise
     const int jpl = g.ncand <= 64 ? 1 : g.ncand <= 128 ? 2 : 4;
     const int W = (g.ncand + 64 * jpl - 1) / (64 * jpl);
 #define SOL_SELECT_CASE(J, T)                                                               \
@@ -396,7 +398,7 @@ hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, fl
     } while (0)
     if (jpl == 1) SOL_SELECT_CASE(1, 16);
     else if (jpl == 2) SOL_SELECT_CASE(2, 16);
-    else SOL_SELECT_CASE(4, 8);
+    else SOL_SELECT_CASE(4, 12);
 #undef SOL_SELECT_CASE
     return hipGetLastError();
 }
