@@ -28,10 +28,19 @@ H3-DataCenter page, policy paragraph; "tokenfactory" = tokenfactory.fast post;
 Routing (steps 1-3) is mirrored in float32 in one fixed order, so the routed
 mask is reproducible bit for bit; attention (step 4) is float64.
 
+Two further parts sit beside the path: packed variable-length batches (each
+sample routed and attended on its own; route_packed, attention_packed) and
+the QK-norm + RoPE producer whose outputs routing pools (qk_norm_rope, a
+float32 mirror in score_ref.c, and qk_norm_rope_f64, its float64 definition).
+
 Parity of the selection rule itself against the published Sol-Attn is
-unpinned: the pages print no rule and no worked example.  Everything else is
-pinned by the tests in tests/test_oracle_*.py (closed forms, brute force on
-tiny inputs, a float64 recomputation of the scores, exact selection sets).
+unpinned: the pages print no rule and no worked example.  So is the choice of
+QK-norm and RoPE variant (per-head RMS normalisation, rotation of channel
+pairs by caller tables): the pages name the fused op and nothing more.
+Everything else is pinned by the tests in tests/test_oracle_*.py (closed
+forms, brute force on tiny inputs, float64 recomputations with error bounds,
+exact selection sets, the defining properties of the normalisation and the
+rotation).
 """
 
 from __future__ import annotations
