@@ -333,6 +333,10 @@ attn_fwd_kernel(
                 lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
             }
         }
+        // keep the row-sum chain here, in the shadow of this half step's
+        // MFMAs: left alone, the compiler sinks it below the mask and rescale
+        // branches, where it runs as a serial chain with the MFMA unit idle
+        asm volatile("" : "+v"(lsum));
     };
     // O^T += V^T P^T
     auto pv = [&](const bf16x8 (&vop)[2][T::DT], const bf16x8 (&p)[2]) {
