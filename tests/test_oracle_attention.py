@@ -83,6 +83,27 @@ def test_lse_merge_equals_single_masked_softmax(B, N, H, D, S, tau):
             np.testing.assert_allclose(L[b, h], logsumexp(z, axis=1), rtol=0, atol=1e-12)
 
 
+def _sweep_cases(n=30, seed=2024):
+    """Seeded sweep: N in 1..300 (no multiple of 64), S in {0, 1, 63, 64, 65, N},
+    D in {64, 128}, H in {1, 3}, tau in {0, 0.3, 1, inf}."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        N = int(rng.integers(1, 301))
+        if N % 64 == 0:
+            continue
+        S = int(rng.choice([0, 1, 63, 64, 65, N]))
+        out.append((1, N, int(rng.choice([1, 3])), int(rng.choice([64, 128])), S,
+                    float(rng.choice([0.0, 0.3, 1.0, math.inf]))))
+    return out
+
+
+@pytest.mark.parametrize("B,N,H,D,S,tau", _sweep_cases())
+def test_lse_merge_seeded_sweep(B, N, H, D, S, tau):
+    """The same check as above over a seeded sweep of small shapes."""
+    test_lse_merge_equals_single_masked_softmax(B, N, H, D, S, tau)
+
+
 @pytest.mark.parametrize("N,S", [(1000, 64), (333, 0), (77, 200)])
 def test_density_one_is_dense_attention(N, S):
     B, H, D = 1, 2, 64
