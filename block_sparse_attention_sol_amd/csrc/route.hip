@@ -151,7 +151,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
     if (ni <= 0) return;
 
     __shared__ float red[TI][kMaxWaves];
-    __shared__ int wcount[TI][JPL * kMaxWaves];
     __shared__ int woffset[TI][JPL * kMaxWaves];
 
     const float* qb = qbar + (int64_t)bh * g.NB * D;
@@ -236,6 +235,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
     // slot) goes to LDS, and each lane sums the attended (row, key) pairs of
     // its selected candidates.
     __shared__ unsigned long long balls[TI][JPL * kMaxWaves];
+    // each lane also keeps its own selections as bits ii * JPL + jj, so the
+    // compaction below rebuilds the ballots instead of reading them back
+    static_assert(TI * JPL <= 64, "one selection bit per (query block, slot)");
+    uint64_t selbits = 0;
     uint32_t keys_local = 0;
 #pragma unroll
     for (int ii = 0; ii < TI; ++ii) {
@@ -248,6 +251,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
             const bool sel = (ii < ni) && jvalid[jj] && (sc[jj][ii] >= thr[ii] || j == i);
             const uint64_t bal = __ballot(sel);
             if (lane == 0) balls[ii][jj * W + wave] = bal;
+            selbits |= (uint64_t)(sel ? 1 : 0) << (ii * JPL + jj);
             const uint32_t keys = (uint32_t)(min(kBlock * j + kBlock, sq.N) - max(kBlock * j, g.S));
             keys_local += sel ? rows * keys : 0u;
         }
@@ -266,16 +270,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
         atomicAdd(&wg_tot[1], (unsigned long long)rows * sq.Ssink);
     }
     __syncthreads();
-    // pass 2: compaction into ascending lists (slot order = block order)
+    // pass 2: compaction into ascending lists (slot order = block order).
+    // Lane e fetches this wave's list offset of (query block e / JPL, slot
+    // e % JPL) in one LDS read; the loop takes it back with readlane.
+    int my_off = 0;
+    if (lane < TI * JPL && lane / JPL < ni) my_off = woffset[lane / JPL][(lane % JPL) * W + wave];
 #pragma unroll
     for (int ii = 0; ii < TI; ++ii) {
         if (ii >= ni) break;
         int16_t* row = idx + ((int64_t)bh * g.NB + i0 + ii) * g.NB;
 #pragma unroll
         for (int jj = 0; jj < JPL; ++jj) {
-            const uint64_t bal = balls[ii][jj * W + wave];
-            if ((bal >> lane) & 1)
-                row[woffset[ii][jj * W + wave] + lanes_below(bal)] = (int16_t)(sq.j0 + jj * slots + tid);
+            const bool sel = (selbits >> (ii * JPL + jj)) & 1;
+            const uint64_t bal = __ballot(sel);
+            const int off = __builtin_amdgcn_readlane(my_off, ii * JPL + jj);
+            if (sel) row[off + lanes_below(bal)] = (int16_t)(sq.j0 + jj * slots + tid);
         }
     }
     const uint32_t wsum = wave_sum(keys_local);
