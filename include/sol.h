@@ -154,9 +154,9 @@ sol_status sol_route(const void* q, const void* k, const sol_desc* desc, float t
  *   blk_idx,  the lists written by sol_route for the same B, N, H and
  *   blk_cnt   sink_len (entries must be ascending candidates in [j0, NB)).
  *   order     optional (NULL: sequence order) schedule written by sol_route;
- *             each row must be a permutation of 0..NB-1 (for a
- *             packed sample: its first ceil(n_b / 64) entries a permutation
- *             of its own blocks, as sol_route writes them).  Query blocks of one
+ *             each row must be a permutation of 0..NB-1 (for a packed
+ *             sample: its first ceil(n_b / 64) entries a permutation of its
+ *             own blocks, as sol_route writes them).  Query blocks of one
  *             (batch, head) are processed in this order; results do not
  *             depend on it.
  *   sink_len  S >= 0 as for sol_route.
