@@ -333,6 +333,22 @@ def main() -> int:
         routed, pairs = int(tot[0]), int(tot[1])
         cand_pairs = H * sum(nb * nc for nb, nc in zip(nbs, ncands))
     flop_eff = 4.0 * D * pairs
+    # tile FLOP: what the attention kernel computes, 64 x 64 tiles including
+    # their masked parts (sink tiles, then each listed block; a listed
+    # straddle block shares the last sink tile)
+    if dense:
+        tile_pairs = H * sum(nb * nb for nb in nbs)
+    else:
+        first = idx[..., 0].cpu().numpy().astype(np.int64)
+        c = cnt.cpu().numpy().astype(np.int64)
+        straddles = 0
+        if w.sink % 64:
+            for bb, (n, nb) in enumerate(zip(lengths, nbs)):
+                if w.sink < n:
+                    straddles += int(((c[bb, :, :nb] > 0) & (first[bb, :, :nb] == w.sink // 64)).sum())
+        nsink_tiles = [(min(w.sink, n) + 63) // 64 for n in lengths]
+        tile_pairs = H * sum(nb * ns for nb, ns in zip(nbs, nsink_tiles)) + routed - straddles
+    flop_tile = 4.0 * D * 64 * 64 * tile_pairs
     rho_route = routed / cand_pairs
     rho_pair = pairs / (H * sum(n * n for n in lengths))
     tflops = flop_eff / (ms_step * 1e-3) / 1e12
@@ -393,6 +409,8 @@ def main() -> int:
             "B": B, "N": N, "H": H, "D": D, "sink": w.sink, "tau": w.tau,
             "route_density": round(rho_route, 6), "pair_density": round(rho_pair, 6),
             "routed_block_pairs": routed, "attended_pairs": pairs,
+            "tile_flop": flop_tile, "effective_flop": flop_eff,
+            "tile_flop_waste": round(1.0 - flop_eff / flop_tile, 5),
             "route_ms": round(t_route, 4), "attn_ms": round(t_attn, 4),
             "warm_ms_per_forward": spread(step_ms), "cold_ms_per_forward": spread(cold_ms),
             **({"producer_ms": round(t_prod, 4), "producer_gbs": round(prod_gbs, 1),
