@@ -162,6 +162,22 @@ def test_producer_packed_batch(sol):
             continue
         nb = r.geom.NB
         compare_masks(gpu_lists_to_mask(idx_h[b:b + 1, :, :nb], cnt_h[b:b + 1, :, :nb], nb), r)
+    # rows after the last sample (T > cu[B]) are neither read into the means
+    # nor written: the same call with 50 extra rows gives the same outputs
+    pad = 50
+    qp, kp = (torch.cat([x, torch.full((pad, H, D), 3.0, dtype=x.dtype, device=x.device)])
+              for x in (q, k))
+    sentinel = torch.full_like(qp, -2.0)
+    qo, ko = sentinel.clone(), sentinel.clone()
+    _, _, wsp = sol.qk_norm_rope_pool(qp, kp, _f32(gq), _f32(gk), EPS, _f32(cos), _f32(sin),
+                                      sink=S, out=(qo, ko), **vk)
+    got_p = sol.route_pooled(qp, wsp, base.tau, S, **vk)
+    torch.cuda.synchronize()
+    T = q.shape[0]
+    assert torch.equal(qo[:T].view(torch.int16), q_out.view(torch.int16))
+    assert torch.equal(ko[:T].view(torch.int16), k_out.view(torch.int16))
+    assert torch.equal(qo[T:], sentinel[T:]) and torch.equal(ko[T:], sentinel[T:])
+    _same_route(got_p, (idx, cnt, totals, order))
 
 
 def test_producer_page_shape(sol):
