@@ -367,7 +367,7 @@ def main() -> int:
     err(f"{args.workload}: {ms_step:.3f} ms/forward (route {t_route:.3f} ms, attention {t_attn:.3f} ms), "
         f"effective {tflops:.1f} TFLOP/s, attention {attn_tflops:.1f} TFLOP/s "
         f"({attn_tflops / PEAK_BF16_TFLOPS:.1%} of bf16 peak), routing "
-        f"{f'{route_gbs:.0f} GB/s' if route_gbs else 'from block means'}; "
+        f"{f'{route_gbs:.0f} GB/s' if route_gbs else ('off' if dense else 'from block means')}; "
         f"route density {rho_route:.4%}, pair density {rho_pair:.4%}; "
         f"wall {wall:.2f} s for {args.steps} steps")
 
