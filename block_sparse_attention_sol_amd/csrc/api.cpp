@@ -189,7 +189,7 @@ sol_status sol_qk_norm_rope_pool(const void* q, const void* k, const sol_desc* d
 
 sol_status sol_route_pooled(const sol_desc* desc, float tau, int32_t sink_len, float scale,
                             int16_t* blk_idx, int32_t* blk_cnt, int64_t* totals, int32_t* order,
-                            const void* workspace, size_t ws_bytes, void* stream) {
+                            void* workspace, size_t ws_bytes, void* stream) {
     sol::Geom g;
     const sol_status st = check_desc(desc, sink_len, &g);
     if (st != SOL_OK) return st;
@@ -207,7 +207,7 @@ sol_status sol_route_pooled(const sol_desc* desc, float tau, int32_t sink_len, f
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SOL_ERR_ALIGN;
     const hipError_t e = sol::launch_route_pooled(g, resolve_scale(scale, g.D), tau, blk_idx, blk_cnt,
                                                   totals, order,
-                                                  static_cast<const float*>(workspace),
+                                                  static_cast<float*>(workspace),
                                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SOL_OK : SOL_ERR_HIP;
 }

@@ -37,12 +37,8 @@ __device__ __forceinline__ void add8(float (&acc)[8], const uint4& w) {
 // chunks, so a lane owning one key block reads its chunk contiguously).
 __global__ __launch_bounds__(256) void pool_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom g,
-    float* __restrict__ qbar, float* __restrict__ kbar, int64_t* __restrict__ totals)
+    float* __restrict__ qbar, float* __restrict__ kbar)
 {
-    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
-        totals[0] = 0;
-        totals[1] = 0;
-    }
     const int blk = blockIdx.x;
     const int b = blockIdx.z >> 1;
     const int is_k = blockIdx.z & 1;
@@ -134,7 +130,7 @@ template <int D, int JPL, int TI>
 __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, Geom g, float scale,
     float tau, int tiles_per_bh, int16_t* __restrict__ idx, int32_t* __restrict__ cnt,
-    int64_t* __restrict__ totals)
+    unsigned long long* __restrict__ wg_part)
 {
     const int work = xcd_remap(blockIdx.x, gridDim.x, tiles_per_bh * g.B * g.H);
     if (work < 0) return;
@@ -148,7 +144,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
     // sample's last block (packed batches) get empty lists
     const int ni = min(TI, sq.NB - i0);
     if (tid < min(TI, g.NB - i0) && tid >= ni) cnt[(int64_t)bh * g.NB + i0 + tid] = 0;
-    if (ni <= 0) return;
+    if (ni <= 0) {                     // nothing routed here: this workgroup's totals are zero
+        if (tid == 0) {
+            wg_part[2 * work] = 0;
+            wg_part[2 * work + 1] = 0;
+        }
+        return;
+    }
 
     __shared__ float red[TI][kMaxWaves];
     __shared__ int woffset[TI][JPL * kMaxWaves];
@@ -162,7 +164,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
     // 32 bytes of k-bar per chunk and each q-bar value feeds JPL FMAs.  Every
     // score is still one FMA chain over d ascending.
     __shared__ __attribute__((aligned(16))) float qs[TI][D];
-    // the workgroup's totals, added to the global ones with one atomic each
+    // the workgroup's totals, written to its own slot of wg_part and summed by
+    // totals_kernel afterwards (one global atomic per workgroup on the same
+    // two counters was 6% of routing time)
     __shared__ unsigned long long wg_tot[2];
     if (tid == 0) {
         wg_tot[0] = 0;
@@ -291,8 +295,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
     if (lane == 0 && wsum != 0) atomicAdd(&wg_tot[1], (unsigned long long)wsum);
     __syncthreads();
     if (tid == 0) {
-        atomicAdd((unsigned long long*)&totals[0], wg_tot[0]);
-        atomicAdd((unsigned long long*)&totals[1], wg_tot[1]);
+        wg_part[2 * work] = wg_tot[0];
+        wg_part[2 * work + 1] = wg_tot[1];
     }
 }
 
@@ -329,9 +333,30 @@ __global__ __launch_bounds__(256) void empty_route_kernel(int32_t* __restrict__ 
     }
 }
 
-// totals start at zero when routing starts from block means written elsewhere
-__global__ __launch_bounds__(64) void clear_totals_kernel(int64_t* __restrict__ totals) {
-    if (threadIdx.x < 2) totals[threadIdx.x] = 0;
+// totals = the sum of the scoring workgroups' partial totals (one workgroup)
+__global__ __launch_bounds__(256) void totals_kernel(const unsigned long long* __restrict__ wg_part,
+                                                     int n, int64_t* __restrict__ totals)
+{
+    __shared__ unsigned long long part[2][256];
+    unsigned long long a = 0, b = 0;
+    for (int i = threadIdx.x; i < n; i += 256) {
+        a += wg_part[2 * i];
+        b += wg_part[2 * i + 1];
+    }
+    part[0][threadIdx.x] = a;
+    part[1][threadIdx.x] = b;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (threadIdx.x < off) {
+            part[0][threadIdx.x] += part[0][threadIdx.x + off];
+            part[1][threadIdx.x] += part[1][threadIdx.x + off];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        totals[0] = (int64_t)part[0][0];
+        totals[1] = (int64_t)part[1][0];
+    }
 }
 
 // Attention schedule: the query blocks of each (batch, head) sorted by list
@@ -389,7 +414,7 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
 template <int D>
 hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, float scale,
                          float tau, int16_t* idx, int32_t* cnt, int64_t* totals,
-                         hipStream_t stream)
+                         unsigned long long* wg_part, hipStream_t stream)
 {
     // candidates per lane: up to 4, so each q-bar value read from LDS feeds
     // up to 4 FMAs; 16 waves x 64 lanes x 4 cover the 4096-candidate limit.
@@ -403,22 +428,28 @@ hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, fl
         const int total = tiles * g.B * g.H;                                                \
         const int grid = round_up(total, kXcds);                                            \
         hipLaunchKernelGGL((score_select_kernel<D, J, T>), dim3(grid), dim3(64 * W), 0,     \
-                           stream, qbar, kbar, g, scale, tau, tiles, idx, cnt, totals);     \
+                           stream, qbar, kbar, g, scale, tau, tiles, idx, cnt, wg_part);    \
+        works = total;                                                                      \
     } while (0)
+    int works = 0;
     if (jpl == 1) SOL_SELECT_CASE(1, 16);
     else if (jpl == 2) SOL_SELECT_CASE(2, 16);
     else SOL_SELECT_CASE(4, 12);
 #undef SOL_SELECT_CASE
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(totals_kernel, dim3(1), dim3(256), 0, stream, wg_part, works, totals);
     return hipGetLastError();
 }
 
 // scores and selection from the block means, then the schedule
 hipError_t select_and_order(const Geom& g, const float* qbar, const float* kbar, float scale,
                             float tau, int16_t* idx, int32_t* cnt, int64_t* totals,
-                            int32_t* order, hipStream_t stream)
+                            int32_t* order, unsigned long long* wg_part, hipStream_t stream)
 {
-    hipError_t e = g.D == 128 ? launch_select<128>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream)
-                              : launch_select<64>(g, qbar, kbar, scale, tau, idx, cnt, totals, stream);
+    hipError_t e = g.D == 128
+        ? launch_select<128>(g, qbar, kbar, scale, tau, idx, cnt, totals, wg_part, stream)
+        : launch_select<64>(g, qbar, kbar, scale, tau, idx, cnt, totals, wg_part, stream);
     if (e != hipSuccess || order == nullptr) return e;
     hipLaunchKernelGGL(order_kernel, dim3(g.B * g.H), dim3(256), (size_t)(g.ncand + 1) * sizeof(int),
                        stream, cnt, g, order);
@@ -427,10 +458,18 @@ hipError_t select_and_order(const Geom& g, const float* qbar, const float* kbar,
 
 }  // namespace
 
+// partial totals of the scoring workgroups: two uint64 per workgroup, at most
+// ceil(NB / 12) workgroups per (batch, head)
+static size_t part_floats(const Geom& g) {
+    const size_t works = (size_t)((g.NB + 11) / 12) * g.B * g.H;
+    return (4 * works + 63) / 64 * 64;
+}
+
 size_t route_ws_floats(const Geom& g) {
-    // qbar and kbar, each B * H * NB * D floats, each rounded to 64 floats
+    // qbar and kbar, each B * H * NB * D floats rounded to 64 floats, then the
+    // scoring workgroups' partial totals
     const size_t one = (size_t)g.B * g.H * g.NB * g.D;
-    return 2 * ((one + 63) / 64 * 64);
+    return 2 * ((one + 63) / 64 * 64) + part_floats(g);
 }
 
 hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale, float tau,
@@ -449,15 +488,15 @@ hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale
     const int lanes = g.H * (g.D / 8);
     dim3 grid(g.NB, (lanes + 255) / 256, g.B * 2);
     hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, stream, (const uint16_t*)q,
-                       (const uint16_t*)k, g, qbar, kbar, totals);
+                       (const uint16_t*)k, g, qbar, kbar);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return select_and_order(g, qbar, kbar, scale, tau, idx, cnt, totals, order, stream);
+    return select_and_order(g, qbar, kbar, scale, tau, idx, cnt, totals, order,
+                            reinterpret_cast<unsigned long long*>(ws + 2 * one), stream);
 }
 
 hipError_t launch_route_pooled(const Geom& g, float scale, float tau, int16_t* idx, int32_t* cnt,
-                               int64_t* totals, int32_t* order, const float* ws,
-                               hipStream_t stream)
+                               int64_t* totals, int32_t* order, float* ws, hipStream_t stream)
 {
     if (g.ncand == 0) {
         const int n = g.B * g.H * g.NB;
@@ -466,10 +505,8 @@ hipError_t launch_route_pooled(const Geom& g, float scale, float tau, int16_t* i
         return hipGetLastError();
     }
     const size_t one = ((size_t)g.B * g.H * g.NB * g.D + 63) / 64 * 64;
-    hipLaunchKernelGGL(clear_totals_kernel, dim3(1), dim3(64), 0, stream, totals);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return select_and_order(g, ws, ws + one, scale, tau, idx, cnt, totals, order, stream);
+    return select_and_order(g, ws, ws + one, scale, tau, idx, cnt, totals, order,
+                            reinterpret_cast<unsigned long long*>(ws + 2 * one), stream);
 }
 
 }  // namespace sol

@@ -70,16 +70,16 @@ __device__ __forceinline__ int xcd_remap(int wg, int grid, int total) {
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 // Routing launch: pool + score/select (+ schedule when order != nullptr).
-// ws holds qbar then kbar.
+// ws holds qbar, kbar, then the scoring workgroups' partial totals.
 hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale, float tau,
                         int16_t* idx, int32_t* cnt, int64_t* totals, int32_t* order, float* ws,
                         hipStream_t stream);
 size_t route_ws_floats(const Geom& g);
 
-// Routing from block means already in ws (written by launch_qk_norm_rope_pool).
+// Routing from block means already in ws (written by launch_qk_norm_rope_pool);
+// the partial totals after them are scratch.
 hipError_t launch_route_pooled(const Geom& g, float scale, float tau, int16_t* idx, int32_t* cnt,
-                               int64_t* totals, int32_t* order, const float* ws,
-                               hipStream_t stream);
+                               int64_t* totals, int32_t* order, float* ws, hipStream_t stream);
 
 // QK-norm + RoPE producer that also writes the block means into ws (the
 // routing workspace layout).  rope_cos / rope_sin may both be null (no RoPE).

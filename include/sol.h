@@ -112,7 +112,9 @@ typedef struct {
 int32_t sol_num_blocks(int32_t N);
 
 /* Device workspace that sol_route needs, in bytes: the pooled queries and
- * keys, 2 * B * H * NB * D float32 plus alignment.  0 for an invalid desc. */
+ * keys, 2 * B * H * NB * D float32, then scratch for the partial totals of
+ * the scoring pass (16 bytes per 12 query blocks per (batch, head)), plus
+ * alignment.  0 for an invalid desc. */
 size_t sol_route_workspace_bytes(const sol_desc* desc);
 
 /*
@@ -249,12 +251,13 @@ sol_status sol_qk_norm_rope_pool(const void* q, const void* k, const sol_desc* d
  * sol_route_pooled -- sol_route from block means already in the workspace
  * (written by sol_qk_norm_rope_pool for the same desc and sink_len): scores,
  * selection, lists, totals and schedule exactly as sol_route computes them
- * on q_out and k_out, without reading Q or K.  Arguments and errors as for
+ * on q_out and k_out, without reading Q or K.  The means are only read; the
+ * workspace's scratch tail is written.  Arguments and errors as for
  * sol_route.
  */
 sol_status sol_route_pooled(const sol_desc* desc, float tau, int32_t sink_len, float scale,
                             int16_t* blk_idx, int32_t* blk_cnt, int64_t* totals, int32_t* order,
-                            const void* workspace, size_t ws_bytes, void* stream);
+                            void* workspace, size_t ws_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* sol_status_str(sol_status status);
