@@ -169,9 +169,9 @@ def main() -> int:
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        err(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
-            f"WORLD_SIZE {world}); the path shards by head across GPUs but no multi-GPU "
-            "run is built here")
+        err(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}, "
+            f"WORLD_SIZE {world}); the path would shard by head across GPUs, but only the "
+            "one-GPU path exists")
         return 2
 
     import numpy as np
