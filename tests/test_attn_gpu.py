@@ -53,7 +53,6 @@ def _run(sol, w: synth.Workload, blocks=None, dense=False, tau=None, inputs=None
     torch.cuda.synchronize()
     got = bf16_tensor_to_f64(o)
     lse = lse.cpu().numpy().astype(np.float64)
-    rows = ~np.isnan(O[..., 0, 0])                 # [B, N]: rows the oracle computed
     if blocks is None:
         ref, gv = O, got
         lref, lgot = L, lse
@@ -68,7 +67,6 @@ def _run(sol, w: synth.Workload, blocks=None, dense=False, tau=None, inputs=None
             lgot.append(lse[b, h, rr.start:rr.stop])
         ref, gv = np.concatenate(ref), np.concatenate(gv)
         lref, lgot = np.concatenate(lref), np.concatenate(lgot)
-    _ = rows
     e = assert_close(gv, ref, f"{w.name} O")
     lerr = float(np.abs(lgot - lref).max())
     log(f"{w.name} LSE max-abs {lerr:.3e}")
@@ -127,6 +125,33 @@ def test_attention_parity_edge_shapes(sol, B, N, H, D, S, tau):
     log(f"attention edge B={B} N={N} H={H} D={D} S={S} tau={tau}")
     w = synth.Workload("edge", B=B, N=N, H=H, D=D, sink=S, tau=tau, kind="field", alpha=1.0,
                        seed=N + S)
+    _run(sol, w)
+
+
+def _sweep_cases(n=12, seed=20261202):
+    """Seeded random shapes with ragged N.  Case c takes sink mode c % 4 (none,
+    random, 951 or the nearest below N, at least N: every key a sink key) and
+    tau mode c % 3 (0: only the maximum and the diagonal, random, +inf: every
+    candidate), so the twelve cases cover every pair of modes."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        N = int(rng.integers(2, 2600))
+        S = [0, int(rng.integers(1, N)), min(951, N - 1), N + int(rng.integers(0, 100))][c % 4]
+        tau = [0.0, float(rng.uniform(0.05, 2.5)), math.inf][c % 3]
+        cases.append((int(rng.integers(1, 3)), N, int(rng.integers(1, 4)),
+                      int(rng.choice([64, 128])), S, tau, 1000 + c))
+    return cases
+
+
+@pytest.mark.parametrize("B,N,H,D,S,tau,seed", _sweep_cases())
+def test_attention_parity_seeded_sweep(sol, B, N, H, D, S, tau, seed):
+    """Routed masks bit-exact and every valid row within tolerance on seeded
+    random shapes (both generators' structure, either head width)."""
+    log(f"attention sweep B={B} N={N} H={H} D={D} S={S} tau={tau:.4g} seed={seed}")
+    kind = "field" if seed % 2 else "tiny"
+    w = synth.Workload("sweep", B=B, N=N, H=H, D=D, sink=S, tau=tau, kind=kind, alpha=1.0,
+                       seed=seed)
     _run(sol, w)
 
 

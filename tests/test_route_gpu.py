@@ -105,6 +105,30 @@ def test_route_parity_edge_shapes(sol, B, N, H, D, S, tau):
     _route_and_check(sol, q, k, N, S, tau, "edge")
 
 
+def _route_sweep_cases(n=8, seed=20261203):
+    """Seeded random routing shapes up to N = 20000 (NB up to 313, so one or
+    two candidate slots per lane), sink mode c % 4 and tau mode c % 2."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        N = int(rng.integers(2, 20000))
+        S = [0, int(rng.integers(1, N)), min(951, N - 1), N + int(rng.integers(0, 100))][c % 4]
+        tau = [float(rng.uniform(0.0, 0.6)), float(rng.uniform(0.6, 3.0))][c % 2]
+        cases.append((int(rng.integers(1, 3)), N, int(rng.integers(1, 5)),
+                      int(rng.choice([64, 128])), S, tau, 2000 + c))
+    return cases
+
+
+@pytest.mark.parametrize("B,N,H,D,S,tau,seed", _route_sweep_cases())
+def test_route_parity_seeded_sweep(sol, B, N, H, D, S, tau, seed):
+    """Lists, counts, totals and the schedule bit-exact on seeded random shapes."""
+    log(f"route sweep B={B} N={N} H={H} D={D} S={S} tau={tau:.4g} seed={seed}")
+    w = synth.Workload("sweep", B=B, N=N, H=H, D=D, sink=S, tau=tau,
+                       kind="field" if seed % 2 else "tiny", alpha=1.0, seed=seed)
+    q, k, _ = synth.make_qkv(w)
+    _route_and_check(sol, q, k, N, S, tau, "sweep")
+
+
 def test_route_strided_views_match_contiguous(sol):
     """Q and K as views of one merged [B, N, 3, H, D] projection."""
     import torch
