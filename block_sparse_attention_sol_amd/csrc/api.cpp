@@ -60,6 +60,10 @@ sol_status check_desc(const sol_desc* d, int32_t sink_len, sol::Geom* g) {
     return SOL_OK;
 }
 
+bool same_io_strides(const sol_desc* d) {
+    return d->qkv_sb == d->o_sb && d->qkv_sn == d->o_sn && d->qkv_sh == d->o_sh;
+}
+
 float resolve_scale(float scale, int D) {
     return scale == 0.0f ? (float)(1.0 / std::sqrt((double)D)) : scale;
 }
@@ -110,6 +114,10 @@ static sol_status attn_common(const void* q, const void* k, const void* v, const
     if (st != SOL_OK) return st;
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return SOL_ERR_ARG;
     if (!dense && (blk_idx == nullptr || blk_cnt == nullptr)) return SOL_ERR_ARG;
+    // O never replaces K or V (other workgroups still read every key row); it
+    // may replace Q when the strides match, since each workgroup reads its
+    // own query rows before it writes them
+    if (o == k || o == v || (o == q && !same_io_strides(desc))) return SOL_ERR_ARG;
     if (std::isnan(scale) || scale < 0.0f || std::isinf(scale)) return SOL_ERR_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
         (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
@@ -143,7 +151,10 @@ sol_status sol_gate_fwd(const void* q, const void* k, const void* v, const sol_d
                         double* stats, void* stream) {
     if (stats == nullptr || o_dense == nullptr) return SOL_ERR_ARG;
     if ((reinterpret_cast<uintptr_t>(stats) & 7u) != 0 || !aligned16(o_dense)) return SOL_ERR_ALIGN;
-    if (o_dense == o_sparse) return SOL_ERR_ARG;
+    // both passes read Q, K and V after the other has written its output
+    if (o_dense == o_sparse || o_sparse == q || o_sparse == k || o_sparse == v || o_dense == q ||
+        o_dense == k || o_dense == v)
+        return SOL_ERR_ARG;
     sol_status st = attn_common(q, k, v, desc, blk_idx, blk_cnt, order, sink_len, scale, o_sparse,
                                 nullptr, false, stream);
     if (st != SOL_OK) return st;
@@ -171,9 +182,7 @@ sol_status sol_qk_norm_rope_pool(const void* q, const void* k, const sol_desc* d
     if ((rope_cos == nullptr) != (rope_sin == nullptr)) return SOL_ERR_ARG;
     if (!(eps >= 0.0f) || std::isinf(eps)) return SOL_ERR_ARG;
     // in place only with identical input and output strides
-    const bool same_strides = desc->qkv_sb == desc->o_sb && desc->qkv_sn == desc->o_sn &&
-                              desc->qkv_sh == desc->o_sh;
-    if ((q_out == q || k_out == k) && !same_strides) return SOL_ERR_ARG;
+    if ((q_out == q || k_out == k) && !same_io_strides(desc)) return SOL_ERR_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) ||
         !aligned16(gamma_q) || !aligned16(gamma_k) || !aligned16(rope_cos) || !aligned16(rope_sin))
         return SOL_ERR_ALIGN;

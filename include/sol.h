@@ -166,6 +166,11 @@ sol_status sol_route(const void* q, const void* k, const sol_desc* desc, float t
  *   o         out, [B, N, H, D] bf16 (strides in desc): for each valid query
  *             row, softmax attention over keys [0, min(S, N)) and the keys
  *             R(j) of every listed block j, rounded to bf16 (nearest even).
+ *             o may be q itself when the O strides equal the Q/K/V strides
+ *             (each query block reads its own rows before it writes them);
+ *             o == k, o == v, or o == q with other strides: SOL_ERR_ARG.
+ *             Other overlaps of o with an input are not detected and give
+ *             unspecified results.
  *   lse       out, optional (NULL to skip), float32 [B, H, N]: natural-log
  *             log-sum-exp of the scaled logits over the same keys.
  */
@@ -191,7 +196,9 @@ sol_status sol_attn_dense_fwd(const void* q, const void* k, const void* v, const
  * settings: reported as maximum, mean and relative L2 error).
  *
  *   o_sparse, o_dense  out, [B, N, H, D] bf16 with the O strides of desc;
- *                      distinct buffers.
+ *                      distinct buffers, neither of them q, k or v (the
+ *                      second pass reads the inputs after the first has
+ *                      written): SOL_ERR_ARG otherwise.
  *   stats     out, device float64 [5], 8-byte aligned: [0] max |s - d|,
  *             [1] sum |s - d|, [2] sum (s - d)^2, [3] sum d^2, [4] number
  *             of elements compared.  Mean = [1] / [4]; relative L2 =

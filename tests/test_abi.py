@@ -157,6 +157,7 @@ def test_route_argument_errors(lib, case, expect):
     ("D32", 2), ("null_v", 1), ("null_idx", 1), ("misaligned_o", 3), ("misaligned_lse", 3),
     ("negative_scale", 1), ("inf_scale", 1), ("odd_o_stride", 3), ("misaligned_order", 3),
     ("packed_batch_stride", 1), ("packed_misaligned_offsets", 3),
+    ("o_is_k", 1), ("o_is_v", 1), ("o_is_q_other_strides", 1),
 ])
 def test_attention_argument_errors(lib, case, expect):
     d = _desc(lib)
@@ -183,7 +184,24 @@ def test_attention_argument_errors(lib, case, expect):
         d = _packed_desc(lib, sb=256000)
     elif case == "packed_misaligned_offsets":
         d = _packed_desc(lib, cu=0x90001)
+    elif case == "o_is_k":
+        kw["o"] = 0x20000
+    elif case == "o_is_v":
+        kw["o"] = 0x30000
+    elif case == "o_is_q_other_strides":
+        d = lib.Desc(1, 1000, 2, 128, 256000, 256, 128, 512000, 512, 128)
+        kw["o"] = 0x10000
     assert _attn(lib, d, **kw) == expect
+
+
+def test_attention_in_place_over_q_with_equal_strides_passes_the_alias_check(lib):
+    # O over Q is legal with equal strides; a misaligned LSE is then the first
+    # rule broken (alignment, not argument), so nothing reaches the device
+    d = _desc(lib)
+    assert _attn(lib, d, o=0x10000, lse=0x70001) == 3
+    st = lib.lib.sol_attn_dense_fwd(0x10000, 0x20000, 0x30000, ctypes.byref(d), ctypes.c_float(0),
+                                    0x20000, None, None)
+    assert st == 1                          # dense output over K
 
 
 def test_dense_argument_errors(lib):
@@ -211,6 +229,10 @@ def test_gate_argument_errors(lib):
     assert gate(stats=None) == 1
     assert gate(od=None) == 1
     assert gate(od=0x60000) == 1            # the two outputs must differ
+    assert gate(os=0x10000) == 1            # neither output may be an input:
+    assert gate(od=0x10000) == 1            # the second pass reads Q, K and V
+    assert gate(os=0x20000) == 1            # after the first one has written
+    assert gate(od=0x30000) == 1
     assert gate(stats=0x80004) == 3         # float64 statistics need 8-byte alignment
     assert gate(od=0x70002) == 3
     assert gate(sink=-1) == 1
