@@ -40,7 +40,7 @@ def _load():
         raise ImportError(f"libsol.so not built at {_LIB_PATH}; run "
                           "`python block_sparse_attention_sol_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(_LIB_PATH)
-    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     dp = ctypes.POINTER(Desc)
     lib.sol_num_blocks.argtypes, lib.sol_num_blocks.restype = [i32], i32
     lib.sol_route_workspace_bytes.argtypes, lib.sol_route_workspace_bytes.restype = [dp], sz
@@ -57,7 +57,6 @@ def _load():
     lib.sol_route_pooled.argtypes = [dp, f32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     lib.sol_route_pooled.restype = ctypes.c_int
     lib.sol_status_str.argtypes, lib.sol_status_str.restype = [ctypes.c_int], ctypes.c_char_p
-    _ = i64
     return lib
 
 
@@ -135,6 +134,33 @@ def _check_qkv(q, k, v=None):
             raise ValueError("Q, K, V must share shape and strides")
 
 
+def _check_buffer(t, dtype, shape, device, name, contiguous=True):
+    """The C ABI takes bare pointers, so the sizes the kernels index by are
+    checked here: a smaller buffer would be read or written past its end."""
+    if (t.dtype != dtype or tuple(t.shape) != tuple(shape) or t.device != device
+            or (contiguous and not t.is_contiguous())):
+        raise ValueError(f"{name} must be a{' contiguous' if contiguous else ''} {dtype} tensor "
+                         f"of shape {tuple(shape)} on {device}")
+
+
+def _check_out(o, q, name="out"):
+    if o.dtype != torch.bfloat16 or o.shape != q.shape or o.device != q.device or o.stride(-1) != 1:
+        raise ValueError(f"{name} must be bf16 with q's shape, on q's device, unit stride along D")
+
+
+def _check_lists(q, blk_idx, blk_cnt, order, cu_seqlens, max_seqlen):
+    B, N, H, _ = _shape(q, cu_seqlens, max_seqlen)
+    NB = num_blocks(N)
+    _check_buffer(blk_idx, torch.int16, (B, H, NB, NB), q.device, "blk_idx")
+    _check_buffer(blk_cnt, torch.int32, (B, H, NB), q.device, "blk_cnt")
+    if order is not None:
+        _check_buffer(order, torch.int32, (B, H, NB), q.device, "order")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 def route_workspace_bytes(q: torch.Tensor, cu_seqlens=None, max_seqlen=None) -> int:
     return int(lib.sol_route_workspace_bytes(ctypes.byref(make_desc(q, None, cu_seqlens,
                                                                     max_seqlen))))
@@ -160,13 +186,15 @@ def route(q: torch.Tensor, k: torch.Tensor, tau: float, sink: int, scale: float 
     desc = make_desc(q, None, cu_seqlens, max_seqlen)
     idx, cnt, totals, order = (route_outputs(q, cu_seqlens, max_seqlen) if out is None
                                else out)
+    _check_lists(q, idx, cnt, order, cu_seqlens, max_seqlen)
+    _check_buffer(totals, torch.int64, (2,), q.device, "totals")
     need = int(lib.sol_route_workspace_bytes(ctypes.byref(desc)))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     st = lib.sol_route(q.data_ptr(), k.data_ptr(), ctypes.byref(desc), ctypes.c_float(tau),
                        int(sink), ctypes.c_float(scale), idx.data_ptr(), cnt.data_ptr(),
                        totals.data_ptr(), order.data_ptr() if order is not None else None,
-                       workspace.data_ptr(), workspace.numel(), _stream(q))
+                       workspace.data_ptr(), _nbytes(workspace), _stream(q))
     _check(st, "sol_route")
     return idx, cnt, totals, order
 
@@ -189,12 +217,10 @@ def attn(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, out=None, ret
     _check_qkv(q, k, v)
     B, N, H, D = _shape(q, cu_seqlens, max_seqlen)
     o = torch.empty_like(q) if out is None else out
+    _check_out(o, q)
     lse = _lse_buffer(q, B, H, N, return_lse, lse_out)
     return_lse = lse is not None
-    if blk_idx.dtype != torch.int16 or blk_cnt.dtype != torch.int32:
-        raise ValueError("blk_idx must be int16 and blk_cnt int32")
-    if order is not None and (order.dtype != torch.int32 or order.shape != blk_cnt.shape):
-        raise ValueError("order must be int32 with blk_cnt's shape")
+    _check_lists(q, blk_idx, blk_cnt, order, cu_seqlens, max_seqlen)
     desc = make_desc(q, o, cu_seqlens, max_seqlen)
     st = lib.sol_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(desc),
                           blk_idx.data_ptr(), blk_cnt.data_ptr(),
@@ -211,6 +237,7 @@ def attn_dense(q, k, v, scale: float = 0.0, out=None, return_lse=False, cu_seqle
     _check_qkv(q, k, v)
     B, N, H, D = _shape(q, cu_seqlens, max_seqlen)
     o = torch.empty_like(q) if out is None else out
+    _check_out(o, q)
     lse = _lse_buffer(q, B, H, N, return_lse, lse_out)
     return_lse = lse is not None
     desc = make_desc(q, o, cu_seqlens, max_seqlen)
@@ -226,6 +253,7 @@ def gate(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, order=None, c
     """Sparse-vs-dense gate: returns (o_sparse, o_dense, stats) with stats a float64
     tensor [max_abs, sum_abs, sum_sq_diff, sum_sq_dense, count] on q's device."""
     _check_qkv(q, k, v)
+    _check_lists(q, blk_idx, blk_cnt, order, cu_seqlens, max_seqlen)
     o_s, o_d = torch.empty_like(q), torch.empty_like(q)
     stats = torch.empty(5, dtype=torch.float64, device=q.device)
     desc = make_desc(q, o_s, cu_seqlens, max_seqlen)
@@ -289,7 +317,7 @@ def qk_norm_rope_pool(q, k, gamma_q, gamma_k, eps: float, rope_cos=None, rope_si
                                    rope_cos.data_ptr() if rope_cos is not None else None,
                                    rope_sin.data_ptr() if rope_sin is not None else None,
                                    int(sink), q_out.data_ptr(), k_out.data_ptr(),
-                                   workspace.data_ptr(), workspace.numel(), _stream(q))
+                                   workspace.data_ptr(), _nbytes(workspace), _stream(q))
     _check(st, "sol_qk_norm_rope_pool")
     return q_out, k_out, workspace
 
@@ -301,10 +329,14 @@ def route_pooled(q, workspace, tau: float, sink: int, scale: float = 0.0, out=No
     desc = make_desc(q, None, cu_seqlens, max_seqlen)
     idx, cnt, totals, order = (route_outputs(q, cu_seqlens, max_seqlen) if out is None
                                else out)
+    _check_lists(q, idx, cnt, order, cu_seqlens, max_seqlen)
+    _check_buffer(totals, torch.int64, (2,), q.device, "totals")
+    if workspace.device != q.device:
+        raise ValueError("workspace must be on q's device")
     st = lib.sol_route_pooled(ctypes.byref(desc), ctypes.c_float(tau), int(sink),
                               ctypes.c_float(scale), idx.data_ptr(), cnt.data_ptr(),
                               totals.data_ptr(), order.data_ptr() if order is not None else None,
-                              workspace.data_ptr(), workspace.numel(), _stream(q))
+                              workspace.data_ptr(), _nbytes(workspace), _stream(q))
     _check(st, "sol_route_pooled")
     return idx, cnt, totals, order
 

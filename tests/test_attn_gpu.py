@@ -344,3 +344,37 @@ def test_sparse_vs_dense_gate(sol, name, N, H):
     log(f"gate {name}: {summ}; oracle l2_rel {ref_l2:.5f} mean_abs {ref_mean:.5f}")
     assert abs(summ["l2_rel"] - ref_l2) <= 5e-3 + 0.02 * ref_l2
     assert abs(summ["mean_abs"] - ref_mean) <= 2e-3 + 0.02 * ref_mean
+
+
+def test_binding_rejects_mis_sized_buffers(sol):
+    """The C ABI takes bare pointers; the binding checks every buffer the kernels
+    index by before the call, so a too-small or mistyped one raises instead of
+    being written past its end.  A workspace of any dtype counts in bytes."""
+    import torch
+    w = replace(synth.WORKLOADS["mid"], N=700, H=2)
+    q, k, v = (to_dev(x) for x in synth.make_qkv(w))
+    idx, cnt, totals, order = sol.route(q, k, w.tau, w.sink)
+    NB = sol.num_blocks(w.N)
+    bad = [
+        dict(out=torch.empty((1, w.N - 1, w.H, w.D), dtype=torch.bfloat16, device="cuda")),
+        dict(out=torch.empty_like(q, dtype=torch.float32)),
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            sol.attn(q, k, v, idx, cnt, w.sink, order=order, **kw)
+        with pytest.raises(ValueError):
+            sol.attn_dense(q, k, v, **kw)
+    with pytest.raises(ValueError):
+        sol.attn(q, k, v, idx[:, :, :NB - 1], cnt, w.sink)
+    with pytest.raises(ValueError):
+        sol.attn(q, k, v, idx, cnt.to(torch.int64), w.sink)
+    with pytest.raises(ValueError):
+        sol.attn(q, k, v, idx, cnt, w.sink, order=order[:, :1])
+    with pytest.raises(ValueError):
+        sol.route(q, k, w.tau, w.sink, out=(idx, cnt, totals[:1], order))
+    # a float32 workspace of the right byte size is accepted
+    nbytes = sol.route_workspace_bytes(q)
+    ws32 = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
+    i2, c2, t2, _ = sol.route(q, k, w.tau, w.sink, workspace=ws32)
+    torch.cuda.synchronize()
+    assert torch.equal(c2, cnt) and torch.equal(t2, totals)
