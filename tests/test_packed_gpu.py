@@ -97,6 +97,55 @@ def test_packed_batch_matches_oracle_all_rows(sol, D):
             assert err <= 2e-3, (b, err)
 
 
+def _packed_sweep_cases(n=6, seed=20261204):
+    """Seeded random packed batches: 2 to 9 samples whose lengths mix empty,
+    sub-block, exact-block and ragged multi-block samples, with a random sink,
+    tau and head width."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        nsamp = int(rng.integers(2, 10))
+        pool = [0, 1, 63, 64, 65, int(rng.integers(2, 64)), int(rng.integers(66, 1500))]
+        lengths = [int(rng.choice(pool)) if rng.random() < 0.4 else int(rng.integers(1, 1800))
+                   for _ in range(nsamp)]
+        if max(lengths) == 0:
+            lengths[0] = 200
+        sink = int(rng.choice([0, 64, int(rng.integers(1, 300))]))
+        tau = float(rng.choice([0.0, float(rng.uniform(0.1, 2.0))]))
+        cases.append((tuple(lengths), int(rng.integers(1, 4)), int(rng.choice([64, 128])), sink,
+                      tau, 3000 + c))
+    return cases
+
+
+@pytest.mark.parametrize("lengths,H,D,S,tau,seed", _packed_sweep_cases())
+def test_packed_batch_seeded_sweep(sol, lengths, H, D, S, tau, seed):
+    """Per-sample lists, counts, totals and schedule bit-exact, O on all rows
+    within tolerance, LSE within 2e-3, on seeded random packed batches."""
+    import torch
+    log(f"packed sweep lengths={list(lengths)} H={H} D={D} S={S} tau={tau:.4g} seed={seed}")
+    base = synth.WORKLOADS["mid"]
+    calls = [replace(base, name=f"sw{i}", N=n, H=H, D=D, sink=S, tau=tau, seed=seed + 17 * i)
+             for i, n in enumerate(lengths)]
+    q_bits, k_bits, v_bits, cu = synth.packed_batch(calls)
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    cud, N = _dev_offsets(cu), max(lengths)
+    idx, cnt, totals, order = sol.route(q, k, tau, S, cu_seqlens=cud, max_seqlen=N)
+    o, lse = sol.attn(q, k, v, idx, cnt, S, return_lse=True, order=order, cu_seqlens=cud,
+                      max_seqlen=N)
+    torch.cuda.synchronize()
+    q32, k32, v32 = (synth.bf16_bits_to_f32(x) for x in (q_bits, k_bits, v_bits))
+    routes = orc.route_packed(q32, k32, cu, S, tau)
+    _check_route(idx.cpu().numpy(), cnt.cpu().numpy(), totals.cpu().numpy(), order.cpu().numpy(),
+                 routes, cu)
+    O, Ls = orc.attention_packed(q32, k32, v32, routes, cu)
+    assert_close(bf16_tensor_to_f64(o), O, "packed sweep O")
+    lse = lse.cpu().numpy()
+    for b, L in enumerate(Ls):
+        n = L.shape[1]
+        if n:
+            assert float(np.abs(lse[b, :, :n] - L).max()) <= 2e-3, b
+
+
 def test_packed_batch_equals_separate_calls_bitwise(sol):
     """Routing lists, counts, totals, O and LSE of the packed call equal the
     fixed-length calls of the samples one by one, bit for bit (the same
