@@ -130,3 +130,57 @@ def test_producer_path_and_dense_replay_in_a_graph(sol):
         assert _lists_equal(idx, cnt, ref[2], ref[3]), rep
         assert torch.equal(totals, ref[4]), rep
     assert int(ref[4][0]) > 0 and np.isfinite(ref[5].float().cpu().numpy()).all()
+
+
+def test_packed_batch_replays_with_new_offsets(sol):
+    """A captured packed-batch forward reads the row offsets from device memory
+    when it runs, so replays with other sample lengths (same B, longest length
+    and row count) need no recapture.  Each replay equals the eager calls on
+    the same offsets bit for bit."""
+    import torch
+    H, D, S, N = 3, 128, 96, 1100
+    base = synth.WORKLOADS["mid"]
+    layouts = [[1000, 0, 640, 97], [64, 1100, 1, 572], [500, 500, 500, 237]]
+    T = sum(layouts[0])
+    assert all(sum(x) == T and max(x) <= N for x in layouts)
+    calls = [replace(base, name=f"g{i}", N=n, H=H, D=D, sink=S, seed=40 + i)
+             for i, n in enumerate(layouts[0])]
+    q_bits, k_bits, v_bits, _ = synth.packed_batch(calls)
+    q, k, v = to_dev(q_bits), to_dev(k_bits), to_dev(v_bits)
+    cu = torch.zeros(len(layouts[0]) + 1, dtype=torch.int32, device="cuda")
+    vk = dict(cu_seqlens=cu, max_seqlen=N)
+    ws = torch.empty(sol.route_workspace_bytes(q, **vk), dtype=torch.uint8, device="cuda")
+    outs = sol.route_outputs(q, **vk)
+    idx, cnt, totals, order = outs
+    o = torch.empty_like(q)
+
+    def set_offsets(lengths):
+        cu.copy_(torch.tensor(np.cumsum([0] + lengths), dtype=torch.int32))
+
+    def step():
+        sol.route(q, k, base.tau, S, workspace=ws, out=outs, **vk)
+        sol.attn(q, k, v, idx, cnt, S, out=o, order=order, **vk)
+
+    refs = []
+    for lengths in layouts:                     # eager results for every layout
+        set_offsets(lengths)
+        o.fill_(0.0)
+        step()
+        torch.cuda.synchronize()
+        refs.append((idx.clone(), cnt.clone(), totals.clone(), o.clone()))
+    set_offsets(layouts[0])
+    graph = _capture(step)
+    for rep in range(6):
+        which = (rep + 1) % len(layouts)
+        set_offsets(layouts[which])
+        o.fill_(0.0)
+        cnt.fill_(-1)
+        totals.fill_(-5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        r_idx, r_cnt, r_tot, r_o = refs[which]
+        assert _lists_equal(idx, cnt, r_idx, r_cnt), rep
+        assert torch.equal(totals, r_tot), rep
+        assert torch.equal(o.view(torch.int16), r_o.view(torch.int16)), rep
+    assert not torch.equal(refs[0][2], refs[1][2])      # the layouts route differently
