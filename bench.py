@@ -122,9 +122,11 @@ def cpu_baseline(w, q_bits, k_bits, v_bits, n_heads: int, n_blocks: int, flop_ef
     t_forward = t_route / len(heads) * w.H + t_attn / n_blocks * w.H * g.NB
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
+        blas_threads = max((p.get("num_threads", 1) for p in pools), default=1)
+        blas_name = ",".join(sorted({str(p.get("internal_api", "?")) for p in pools})) or "?"
     except Exception:
-        blas_threads = os.cpu_count() or 1
+        blas_threads, blas_name = os.cpu_count() or 1, "unknown"
     score_threads = min(8, os.cpu_count() or 1)
     return {
         "value": flop_eff / t_forward / 1e12,
@@ -136,7 +138,8 @@ def cpu_baseline(w, q_bits, k_bits, v_bits, n_heads: int, n_blocks: int, flop_ef
                    f"({flops / 1e9:.1f} GFLOP) in {t_attn:.2f} s; rate for the whole forward = "
                    f"effective FLOP / (route time per head x {w.H} + attention time per block x "
                    f"{w.H * g.NB}) = {t_forward:.0f} s per forward; host cpu_count "
-                   f"{os.cpu_count()}"),
+                   f"{os.cpu_count()}, BLAS {blas_name} with {blas_threads} threads, routing "
+                   f"scores in {score_threads} threads"),
     }
 
 
