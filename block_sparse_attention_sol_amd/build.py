@@ -10,6 +10,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -38,19 +39,27 @@ def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
+    def compile_one(src):
         obj = os.path.join(objdir, src + f".{os.getpid()}.o")
         cmd = [hipcc, *HIPCC_FLAGS, *EXTRA.get(src, []), f"-I{INCLUDE}", f"-I{CSRC}", "-c", "-o",
                obj, os.path.join(CSRC, src)]
         cmd.remove("-shared")
         if verbose:
             print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True)
+        return src, obj, subprocess.run(cmd, capture_output=True, text=True)
+
+    # the sources compile independently; at most MAX_JOBS (or the CPU count) at once
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        results = list(pool.map(compile_one, SOURCES))
+    objs = [obj for _, obj, _ in results]
+    for src, obj, res in results:
         if res.returncode != 0:
             sys.stderr.write(res.stdout + res.stderr)
+            for o in objs:
+                if os.path.exists(o):
+                    os.remove(o)
             raise RuntimeError(f"hipcc failed on {src}")
-        objs.append(obj)
     tmp = LIB + f".tmp{os.getpid()}"
     cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
