@@ -28,3 +28,42 @@ def test_world_size_above_one_is_refused():
     r = _bench("--steps", "1", "--warmup", "0", env=env)
     assert r.returncode == 2
     assert "WORLD_SIZE 4" in r.stderr
+
+
+def _counter_csv(path, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value"])
+        w.writeheader()
+        for i, (kernel, counter, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": kernel, "Counter_Name": counter,
+                        "Counter_Value": value})
+
+
+def test_traffic_record_scales_by_the_copy_calibration(tmp_path, monkeypatch):
+    """roofline.traffic: FETCH_SIZE / WRITE_SIZE of the attention kernel (KiB per
+    dispatch, averaged) scaled by what the same counters read for a plain copy
+    of known size; the record holds only while the kernel source is unchanged."""
+    sys.path.insert(0, ROOT)
+    import bench
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    attn = "void sol::(anonymous namespace)::attn_fwd_kernel<128, false>(...)"
+    other = "void sol::(anonymous namespace)::pool_kernel(...)"
+    copy = "__amd_rocclr_copyBuffer"
+    f, w, cf, cw = (str(tmp_path / n) for n in ("f.csv", "w.csv", "cf.csv", "cw.csv"))
+    _counter_csv(f, [(attn, "FETCH_SIZE", 1000.0), (attn, "FETCH_SIZE", 3000.0),
+                     (other, "FETCH_SIZE", 9e9)])
+    _counter_csv(w, [(attn, "WRITE_SIZE", 500.0), (other, "WRITE_SIZE", 9e9)])
+    copy_bytes = 1 << 20                       # a copy of 1 MiB reads and writes 1 MiB
+    _counter_csv(cf, [(copy, "FETCH_SIZE", 512.0)])     # fetch counter reads half: scale 2
+    _counter_csv(cw, [(copy, "WRITE_SIZE", 1024.0)])    # write counter exact: scale 1
+    rec = bench.record_traffic(f, w, cf, cw, copy_bytes=copy_bytes)
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["hbm_bytes_per_launch"] == int(2000.0 * 1024 * 2 + 500.0 * 1024)
+    assert bench.measured_traffic() == rec["hbm_bytes_per_launch"]
+    # a record taken on another kernel source is ignored (traffic reported as null)
+    import json
+    stale = dict(rec, attn_src_sha256_16="0" * 16)
+    (tmp_path / "traffic.json").write_text(json.dumps(stale))
+    assert bench.measured_traffic() is None
