@@ -30,8 +30,9 @@ mask is reproducible bit for bit; attention (step 4) is float64.
 
 Two further parts sit beside the path: packed variable-length batches (each
 sample routed and attended on its own; route_packed, attention_packed) and
-the QK-norm + RoPE producer whose outputs routing pools (qk_norm_rope, a
-float32 mirror in score_ref.c, and qk_norm_rope_f64, its float64 definition).
+the QK-norm + RoPE producer whose outputs routing pools (qk_norm_rope, its
+float32 definition in score_ref.c, and qk_norm_rope_f64, the same in float64
+without rounding).
 
 Parity of the selection rule itself against the published Sol-Attn is
 unpinned: the pages print no rule and no worked example.  So is the choice of
@@ -63,7 +64,7 @@ _LIB = os.path.join(_HERE, "_score_ref.so")
 
 # --------------------------------------------------------------------------- C part
 def build_c(force: bool = False) -> str:
-    """Compile the float32 score mirror (plain C, gcc) next to its source."""
+    """Compile the float32 scores and producer (plain C, gcc) next to their source."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + f".tmp{os.getpid()}"
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
@@ -442,7 +443,9 @@ def qk_norm_rope_f64(x: np.ndarray, gamma: np.ndarray, eps: float, cos=None, sin
 
 
 def qk_norm_rope(x_bits: np.ndarray, gamma: np.ndarray, eps: float, cos=None, sin=None):
-    """The float32 mirror (score_ref.c): [B, N, H, D] bf16 bits -> bf16 bits."""
+    """The float32 definition (score_ref.c: one ascending running sum of squares,
+    then the normalisation and rotation, each step one float32 rounding):
+    [B, N, H, D] bf16 bits -> bf16 bits."""
     B, N, H, D = x_bits.shape
     lib = _clib()
     g = np.ascontiguousarray(gamma, np.float32)
@@ -461,7 +464,7 @@ def qk_norm_rope(x_bits: np.ndarray, gamma: np.ndarray, eps: float, cos=None, si
 
 
 def qk_norm_rope_packed(x_bits: np.ndarray, cu, gamma, eps: float, cos=None, sin=None):
-    """The mirror on a packed [T, H, D] batch: positions restart at 0 in every sample;
+    """qk_norm_rope on a packed [T, H, D] batch: positions restart at 0 in every sample;
     rows outside the samples are returned unchanged."""
     out = x_bits.copy()
     cu = [int(c) for c in cu]

@@ -1,5 +1,5 @@
 /*
- * CPU oracle, float32 mirrors: pooled block scores, and the QK-norm + RoPE
+ * CPU oracle, float32 definitions: pooled block scores, and the QK-norm + RoPE
  * producer (second half of this file).  TEST INFRASTRUCTURE ONLY: nothing on
  * the product path links or calls this file.
  *
@@ -37,15 +37,16 @@ void oracle_block_scores(const float *qbar, const float *kbar, int64_t nq, int64
 }
 
 /*
- * QK-norm + RoPE, float32 mirror.  QK-norm plus RoPE is the fused op the
+ * QK-norm + RoPE in float32.  QK-norm plus RoPE is the fused op the
  * tokenfactory.fast post ("Custom kernels") names right before attention; the
  * pages define neither, so the reading is per-head RMS normalisation with a
  * weight per channel, then the rotation of channel pairs (2i, 2i + 1) by the
  * angle whose cosine and sine the caller tables give for the row's position.
- * One row x of D bf16 values, written step by step in one fixed float32 order:
+ * One row x of D bf16 values, each step one float32 rounding, in this order:
  *
- *   p[c]  = fmaf chain over the 8 channels 8c .. 8c+7 ascending of x*x, from +0
- *   ss    = balanced binary tree of p[0 .. D/8-1] in index order
+ *   ss    = +0;  for d = 0 .. D-1 ascending:  ss = fmaf(x[d], x[d], ss)
+ *           (the plain running sum of squares: a bf16 square is exact in
+ *           float32, so the fused and the unfused step round alike)
  *   r     = 1 / sqrtf(fmaf(ss, 1/D, eps))
  *   y[d]  = (x[d] * r) * gamma[d]
  *   o[2i] = fmaf(y[2i], c, -(y[2i+1] * s)),  o[2i+1] = fmaf(y[2i], s, y[2i+1] * c)
@@ -74,22 +75,14 @@ static uint16_t f32_to_bf16_rne(float f)
 void oracle_qk_norm_rope(const uint16_t *x, int64_t rows, int64_t d, const float *gamma,
                          float eps, const float *cosv, const float *sinv, uint16_t *out)
 {
-    const int64_t nch = d / 8;
     for (int64_t t = 0; t < rows; ++t) {
         const uint16_t *xr = x + t * d;
-        float p[64];
-        for (int64_t c = 0; c < nch; ++c) {
-            float acc = 0.0f;
-            for (int64_t e = 0; e < 8; ++e) {
-                const float v = bf16_to_f32(xr[8 * c + e]);
-                acc = fmaf(v, v, acc);
-            }
-            p[c] = acc;
+        float ss = 0.0f;
+        for (int64_t e = 0; e < d; ++e) {
+            const float v = bf16_to_f32(xr[e]);
+            ss = fmaf(v, v, ss);
         }
-        for (int64_t w = 1; w < nch; w *= 2)
-            for (int64_t c = 0; c + w < nch; c += 2 * w)
-                p[c] = p[c] + p[c + w];
-        const float r = 1.0f / sqrtf(fmaf(p[0], 1.0f / (float)d, eps));
+        const float r = 1.0f / sqrtf(fmaf(ss, 1.0f / (float)d, eps));
         float y[512];
         for (int64_t e = 0; e < d; ++e)
             y[e] = (bf16_to_f32(xr[e]) * r) * gamma[e];

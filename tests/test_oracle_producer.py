@@ -1,8 +1,9 @@
 """Pins for the oracle's QK-norm + RoPE producer.
 
-The float32 mirror (score_ref.c) is checked against the float64 definition
-within a rounding bound derived from the arithmetic, on inputs where each
-term matters (eps included); the float64 definition is checked against
+The float32 definition (score_ref.c) is checked against the float64
+definition within a rounding bound derived from the arithmetic, on inputs
+where each term matters (eps included), and its order of summation against a
+hand-worked case where every other order gives other bits; the float64 definition is checked against
 closed forms and the defining properties of the two operations: a constant
 row normalises to its sign, the RMS of a normalised row is one, a rotation
 keeps each pair's length, the quarter turn and the identity act as stated,
@@ -54,6 +55,42 @@ def test_mirror_within_rounding_of_the_definition(D, scale, eps, rope):
     assert (np.abs(got - ref) <= tol).all(), float((np.abs(got - ref) - tol).max())
     # and the mirror is really rounding: most values sit well inside half an ulp
     assert np.mean(np.abs(got - ref) <= 0.5 * _half_ulp_bf16(ref) + err32) > 0.4
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_sum_of_squares_order_exact(D):
+    """The sum of squares is one running float32 sum over d ascending from +0.
+
+    Worked by hand (u = 2^-24; g = 1 + 2^-8 + 2^-20 for every channel, eps 0,
+    no rotation).  Row A puts the large values first: x = 4096 at d = 0
+    (and d = 1 when D = 128), every other x = 1.  Ascending, ss reaches
+    2^24 (D 64) or 2^25 (D 128), and every following 1 is absorbed (at
+    2^24 an added 1 is a tie that rounds to the even 2^24), so
+    ss / D = 2^18, r = 2^-9 exactly, and a channel with x = 1 gives
+    y = 2^-9 g, just above the bf16 midpoint 2^-9 (1 + 2^-8): it rounds
+    up to 2^-9 (1 + 2^-7); x = 4096 gives 8 g -> 8 (1 + 2^-7).  Row B puts
+    the large values last.  Ascending, the ones add up first (D - 1 or
+    D - 2 of them), the large squares then round the sum to 2^24 + 64 or
+    2^25 + 128, so ss / D = 2^18 + 1, sqrt rounds to 512 + 2^-10,
+    r = 2^-9 (1 - 2^-19), and y = r g lands 2^-29 below the midpoint: x = 1
+    gives 2^-9, x = 4096 gives 8.
+
+    Other orders give other bits: partial sums of 8-channel chunks added
+    as a tree make row A's ss 2^24 + 56 (or 2^25 + 120), which rounds
+    every x = 1 channel down; descending order makes row B's ss 2^24 (or
+    2^25), which rounds them up.
+    """
+    nbig = 1 if D == 64 else 2
+    x = np.ones((1, 2, 1, D), np.float32)
+    x[0, 0, 0, :nbig] = 4096.0
+    x[0, 1, 0, D - nbig:] = 4096.0
+    g = np.full(D, 1 + 2.0 ** -8 + 2.0 ** -20, np.float32)
+    out = synth.bf16_bits_to_f32(orc.qk_norm_rope(_bits(x), g, 0.0)).astype(np.float64)
+    up, big_up = 2.0 ** -9 * (1 + 2.0 ** -7), 8.0 * (1 + 2.0 ** -7)
+    np.testing.assert_array_equal(out[0, 0, 0, :nbig], big_up)
+    np.testing.assert_array_equal(out[0, 0, 0, nbig:], up)
+    np.testing.assert_array_equal(out[0, 1, 0, D - nbig:], 8.0)
+    np.testing.assert_array_equal(out[0, 1, 0, : D - nbig], 2.0 ** -9)
 
 
 def test_eps_and_weights_change_the_result():
