@@ -10,9 +10,10 @@ import numpy as np
 import synth
 from oracle import oracle as orc
 
-# Tolerance for the bf16 output O against the float64 oracle: max-abs 1e-2
-# on top of the half-ulp rounding to bf16 that an exact result already pays
-# (one bf16 ulp is 2^-6 = 0.0156 for |O| in [2, 4)), and L2-relative 5e-3.
+# Tolerance for the bf16 output O against the float64 oracle: the raw
+# max-abs error <= 1e-2 and L2-relative <= 5e-3.  How much of the error is the
+# bf16 rounding an exact result pays anyway (half an ulp, 2^-9 |O|) is logged
+# for information only.
 MAX_ABS = 1e-2
 L2_REL = 5e-3
 
@@ -63,14 +64,19 @@ def check_schedule(order, cnt):
             assert np.all(np.diff(cnt[b, h][o]) <= 0), (b, h)
 
 
-def compare_masks(gpu_sel: np.ndarray, r: orc.Route) -> None:
-    """Bit-exact mask parity; a mismatch is allowed only on a listed near-tie."""
+def compare_masks(gpu_sel: np.ndarray, r: orc.Route, what: str = "mask") -> int:
+    """Bit-exact mask parity: zero mismatches allowed.  Both sides compute the
+    scores in the same float32 order, so even a near-tie (|s - T| within 1e-6
+    relative) must select alike; the near-ties are counted and logged so that
+    a test shows how close the threshold came.  Returns that count."""
+    ties = orc.tie_list(r.scores, r.thresh, r.geom)
     diff = np.argwhere(gpu_sel != r.sel)
-    if len(diff) == 0:
-        return
-    ties = {tuple(x) for x in orc.tie_list(r.scores, r.thresh, r.geom).tolist()}
-    bad = [tuple(x) for x in diff.tolist() if tuple(x) not in ties]
-    assert not bad, f"{len(bad)} mask mismatches outside the tie list, first {bad[:5]}"
+    tie_set = {tuple(x) for x in ties.tolist()}
+    on_ties = sum(tuple(x) in tie_set for x in diff.tolist())
+    log(f"{what}: {int(r.sel.sum())} selected pairs, {len(ties)} near-ties listed, "
+        f"{len(diff)} mismatches ({on_ties} of them on a near-tie)")
+    assert len(diff) == 0, f"{len(diff)} mask mismatches, first {diff[:5].tolist()}"
+    return len(ties)
 
 
 def errors(got: np.ndarray, ref: np.ndarray) -> dict:
@@ -85,7 +91,7 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str = "") -> dict:
     assert np.isfinite(got).all(), f"{what}: non-finite GPU output"
     e = errors(got, ref)
     log(f"{what}: {e}")
-    assert e["max_abs_beyond_rounding"] <= MAX_ABS and e["l2_rel"] <= L2_REL, f"{what}: {e}"
+    assert e["max_abs"] <= MAX_ABS and e["l2_rel"] <= L2_REL, f"{what}: {e}"
     return e
 
 
