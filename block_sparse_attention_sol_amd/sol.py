@@ -251,11 +251,12 @@ def attn_dense(q, k, v, scale: float = 0.0, out=None, return_lse=False, cu_seqle
 def gate(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, order=None, cu_seqlens=None,
          max_seqlen=None):
     """Sparse-vs-dense gate: returns (o_sparse, o_dense, stats) with stats a float64
-    tensor [max_abs, sum_abs, sum_sq_diff, sum_sq_dense, count] on q's device."""
+    tensor [max_abs, sum_abs, sum_sq_diff, sum_sq_dense, count, mean_abs, l2_rel]
+    on q's device, all computed by the library."""
     _check_qkv(q, k, v)
     _check_lists(q, blk_idx, blk_cnt, order, cu_seqlens, max_seqlen)
     o_s, o_d = torch.empty_like(q), torch.empty_like(q)
-    stats = torch.empty(5, dtype=torch.float64, device=q.device)
+    stats = torch.empty(7, dtype=torch.float64, device=q.device)
     desc = make_desc(q, o_s, cu_seqlens, max_seqlen)
     st = lib.sol_gate_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(desc),
                           blk_idx.data_ptr(), blk_cnt.data_ptr(),
@@ -264,13 +265,6 @@ def gate(q, k, v, blk_idx, blk_cnt, sink: int, scale: float = 0.0, order=None, c
                           _stream(q))
     _check(st, "sol_gate_fwd")
     return o_s, o_d, stats
-
-
-def gate_summary(stats) -> dict:
-    """max-abs, mean-abs and relative-L2 error from sol_gate_fwd's statistics."""
-    s = stats.cpu().tolist()
-    return {"max_abs": s[0], "mean_abs": s[1] / max(s[4], 1.0),
-            "l2_rel": math.sqrt(s[2] / s[3]) if s[3] > 0 else 0.0}
 
 
 def forward(q, k, v, tau: float, sink: int, scale: float = 0.0, return_lse=False,
@@ -292,8 +286,10 @@ def qk_norm_rope_pool(q, k, gamma_q, gamma_k, eps: float, rope_cos=None, rope_si
     workspace to route_pooled().  ``out`` = (q_out, k_out) may be (q, k) (in place).
     gamma_* are float32 [D]; rope_cos / rope_sin float32 [N, D/2] or None."""
     _check_qkv(q, k)
-    desc = make_desc(q, None if out is None else out[0], cu_seqlens, max_seqlen)
+    # the outputs first: their strides (not q's) are the descriptor's O strides;
+    # empty_like of a strided view (say of a merged QKV projection) is dense
     q_out, k_out = (torch.empty_like(q), torch.empty_like(k)) if out is None else out
+    desc = make_desc(q, q_out, cu_seqlens, max_seqlen)
     for t in (q_out, k_out):
         if (not t.is_cuda or t.dtype != torch.bfloat16 or t.shape != q.shape
                 or t.stride() != q_out.stride()):

@@ -135,6 +135,31 @@ def test_producer_strided_views(sol):
     assert torch.equal(outm[:, :, 1].contiguous().view(torch.int16), k_out.view(torch.int16))
 
 
+def test_producer_merged_views_default_outputs(sol):
+    """Q and K as views of one merged [B, N, 3, H, D] projection with out=None:
+    the binding allocates dense outputs and must describe them by their own
+    strides (not the inputs'), so outputs and block means equal the
+    contiguous call's bit for bit."""
+    import torch
+    w = replace(synth.WORKLOADS["mid"], N=700, H=4)
+    q_bits, k_bits, _ = synth.make_qkv(w)
+    gq, gk, cos, sin = _weights(w.N, w.D, True)
+    args = (_f32(gq), _f32(gk), EPS, _f32(cos), _f32(sin))
+    q, k = to_dev(q_bits), to_dev(k_bits)
+    merged = torch.empty((1, w.N, 3, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    merged[:, :, 0] = q
+    merged[:, :, 1] = k
+    qv, kv = merged[:, :, 0], merged[:, :, 1]
+    q_m, k_m, ws_m = sol.qk_norm_rope_pool(qv, kv, *args, sink=w.sink)
+    assert q_m.is_contiguous() and k_m.is_contiguous()
+    q_c, k_c, ws_c = sol.qk_norm_rope_pool(q, k, *args, sink=w.sink)
+    torch.cuda.synchronize()
+    assert torch.equal(q_m.view(torch.int16), q_c.view(torch.int16))
+    assert torch.equal(k_m.view(torch.int16), k_c.view(torch.int16))
+    # the block means: the routing from them is the same bit for bit
+    _same_route(sol.route_pooled(qv, ws_m, w.tau, w.sink), sol.route_pooled(q, ws_c, w.tau, w.sink))
+
+
 def test_producer_packed_batch(sol):
     import torch
     lengths, H, D, S = [1000, 0, 64, 777, 2053, 130, 96], 3, 128, 96
