@@ -96,8 +96,12 @@ def record_traffic(fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_wri
     return rec
 
 
-def cpu_baseline(w, q_bits, k_bits, v_bits, n_heads: int, n_blocks: int, flop_eff: float):
-    """Time the oracle (as it stands) on a bounded sample of the same workload."""
+def cpu_baseline(w, q_bits, k_bits, v_bits, n_heads: int):
+    """Time the oracle (as it stands) on a whole, stated slice of the same
+    workload: the complete forward -- routing (float32 pool, score, select) and
+    float64 sink + routed attention of every query block -- of the first
+    n_heads heads.  The value is that slice's effective FLOP over its measured
+    wall time; nothing is extrapolated."""
     import numpy as np
 
     import synth
@@ -108,18 +112,11 @@ def cpu_baseline(w, q_bits, k_bits, v_bits, n_heads: int, n_blocks: int, flop_ef
     t0 = time.perf_counter()
     r = orc.route(qh, kh, w.N, w.sink, w.tau)
     t_route = time.perf_counter() - t0
-    g = r.geom
-    rng = np.random.default_rng(0)
-    blocks = [(0, int(rng.integers(len(heads))), int(rng.integers(g.NB))) for _ in range(n_blocks)]
-    flops = 0
-    for b, h, i in blocks:
-        keys = g.Ssink + sum(len(g.r_keys(j)) for j in np.nonzero(r.sel[b, h, i])[0])
-        flops += 4 * w.D * len(g.q_rows(i)) * keys
     t0 = time.perf_counter()
-    orc.attention(qh, kh, vh, r.sel, g, blocks=blocks)
+    orc.attention(qh, kh, vh, r.sel, r.geom)
     t_attn = time.perf_counter() - t0
-    # whole forward at these rates: routing per head x H, attention per query block x H*NB
-    t_forward = t_route / len(heads) * w.H + t_attn / n_blocks * w.H * g.NB
+    flops = 4.0 * w.D * r.attended_pairs
+    t_all = t_route + t_attn
     try:
         from threadpoolctl import threadpool_info
         pools = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
@@ -129,18 +126,47 @@ def cpu_baseline(w, q_bits, k_bits, v_bits, n_heads: int, n_blocks: int, flop_ef
         blas_threads, blas_name = os.cpu_count() or 1, "unknown"
     score_threads = min(8, os.cpu_count() or 1)
     return {
-        "value": flop_eff / t_forward / 1e12,
+        "value": flops / t_all / 1e12,
         "unit": "TFLOP/s",
         "cores": int(max(blas_threads, score_threads)),
         "kind": "oracle",
-        "sample": (f"oracle routing (float32 pool/score/select) of heads {heads} in "
-                   f"{t_route:.2f} s and float64 attention of {n_blocks} seeded query blocks "
-                   f"({flops / 1e9:.1f} GFLOP) in {t_attn:.2f} s; rate for the whole forward = "
-                   f"effective FLOP / (route time per head x {w.H} + attention time per block x "
-                   f"{w.H * g.NB}) = {t_forward:.0f} s per forward; host cpu_count "
+        "sample": (f"the whole forward of heads {heads[0]}-{heads[-1]} ({n_heads} of {w.H}) of "
+                   f"the same workload, measured: routing of those heads in {t_route:.2f} s, "
+                   f"float64 attention of all {n_heads * r.geom.NB} of their query blocks "
+                   f"({flops / 1e9:.1f} effective GFLOP) in {t_attn:.2f} s; value = effective "
+                   f"FLOP / measured time ({t_all:.1f} s), no extrapolation; host cpu_count "
                    f"{os.cpu_count()}, BLAS {blas_name} with {blas_threads} threads, routing "
                    f"scores in {score_threads} threads"),
+        "seconds": round(t_all, 2),
+        "effective_flop": flops,
     }
+
+
+def trace_summary(csv_path: str, warmup: int, steps: int) -> dict:
+    """Per-kernel durations from a rocprofv3 --kernel-trace CSV of one bench run.
+
+    Each forward launches each of its kernels once, so the n-th dispatch of a
+    kernel (in start order) belongs to forward n: the first `warmup` are the
+    warm-ups, the next `steps` the timed back-to-back forwards of the bench
+    line, and the next `steps` the cold-cache forwards."""
+    import csv
+    import statistics
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    out = {}
+    for name, d in per.items():
+        d.sort()
+        us = [(e - b) / 1e3 for b, e in d]
+        warm = us[warmup:warmup + steps]
+        cold = us[warmup + steps:warmup + 2 * steps]
+        out[name] = {"calls": len(us), "mean_all_us": round(statistics.mean(us), 2),
+                     "mean_timed_us": round(statistics.mean(warm), 2) if warm else None,
+                     "median_timed_us": round(statistics.median(warm), 2) if warm else None,
+                     "mean_cold_us": round(statistics.mean(cold), 2) if cold else None,
+                     "min_us": round(min(us), 2), "max_us": round(max(us), 2)}
+    return out
 
 
 def main() -> int:
@@ -154,8 +180,11 @@ def main() -> int:
                          "H = 14) packed into one call; page_fused: the pages' shape with the "
                          "QK-norm + RoPE producer in front, routing from its block means")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=2048)
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=4,
+                    help="heads whose whole forward the oracle baseline times")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="per-kernel durations (all, timed window, cold window) from a rocprofv3 "
+                         "kernel-trace CSV of a bench run with the same --warmup/--steps; no GPU")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (for scaling "
                          "the HBM counters FETCH_SIZE / WRITE_SIZE) and exit")
@@ -166,6 +195,9 @@ def main() -> int:
     ap.add_argument("--copy-bytes", type=int, default=1 << 30,
                     help="size of the copy behind COPY_*_CSV (default 1 GiB)")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(json.dumps(trace_summary(args.trace_summary, args.warmup, args.steps), indent=1))
+        return 0
     if args.record_traffic:
         rec = record_traffic(*args.record_traffic, copy_bytes=args.copy_bytes)
         print(json.dumps(rec))
@@ -354,6 +386,11 @@ def main() -> int:
     flop_tile = 4.0 * D * 64 * 64 * tile_pairs
     rho_route = routed / cand_pairs
     rho_pair = pairs / (H * sum(n * n for n in lengths))
+    # block density: block pairs (i, j) with at least one attended key, sink or
+    # routed, over all B H NB^2 block pairs (the straddle block counts once);
+    # these are exactly the 64 x 64 tiles the kernel computes
+    block_den = H * sum(nb * nb for nb in nbs)
+    rho_block = tile_pairs / block_den
     tflops = flop_eff / (ms_step * 1e-3) / 1e12
     attn_tflops = flop_eff / (t_attn * 1e-3) / 1e12
     route_bytes = (sum(n * H * D * 2 + max(n - w.sink, 0) * H * D * 2 for n in lengths)
@@ -371,7 +408,8 @@ def main() -> int:
         f"effective {tflops:.1f} TFLOP/s, attention {attn_tflops:.1f} TFLOP/s "
         f"({attn_tflops / PEAK_BF16_TFLOPS:.1%} of bf16 peak), routing "
         f"{f'{route_gbs:.0f} GB/s' if route_gbs else ('off' if dense else 'from block means')}; "
-        f"route density {rho_route:.4%}, pair density {rho_pair:.4%}; "
+        f"route density {rho_route:.4%}, block density {rho_block:.4%}, pair density "
+        f"{rho_pair:.4%}; "
         f"wall {wall:.2f} s for {args.steps} steps")
 
     err(f"per forward: warm median {np.median(step_ms):.3f} ms (p10 {np.percentile(step_ms, 10):.3f}, "
@@ -410,7 +448,10 @@ def main() -> int:
         "config": {
             "workload": desc,
             "B": B, "N": N, "H": H, "D": D, "sink": w.sink, "tau": w.tau,
-            "route_density": round(rho_route, 6), "pair_density": round(rho_pair, 6),
+            "route_density": round(rho_route, 6), "block_density": round(rho_block, 6),
+            "pair_density": round(rho_pair, 6),
+            "densities_exact": {"route": [routed, cand_pairs], "block": [tile_pairs, block_den],
+                                "pair": [pairs, H * sum(n * n for n in lengths)]},
             "routed_block_pairs": routed, "attended_pairs": pairs,
             "tile_flop": flop_tile, "effective_flop": flop_eff,
             "tile_flop_waste": round(1.0 - flop_eff / flop_tile, 5),
@@ -434,8 +475,7 @@ def main() -> int:
         err("cpu baseline: timed on the default (pages' shape) workload only")
     if not args.no_cpu_baseline and not packed and not producer:
         t0 = time.perf_counter()
-        rec["cpu_baseline"] = cpu_baseline(w, q_bits, k_bits, v_bits, args.cpu_heads, args.cpu_blocks,
-                                           flop_eff)
+        rec["cpu_baseline"] = cpu_baseline(w, q_bits, k_bits, v_bits, args.cpu_heads)
         err(f"cpu baseline took {time.perf_counter() - t0:.1f} s")
     if packed:
         rec["config"]["sample_lengths"] = lengths

@@ -5,6 +5,6 @@ binding over it.  Importing the package loads libsol.so and raises ImportError
 when it has not been built.
 """
 from .sol import (BLOCK, Desc, SolError, attn, attn_dense, default_scale, forward,  # noqa: F401
-                  gate, gate_summary, make_desc, num_blocks, packed_offsets,
+                  gate, make_desc, num_blocks, packed_offsets,
                   qk_norm_rope_pool, route, route_outputs, route_pooled,
                   route_workspace_bytes, status_str)

@@ -8,9 +8,11 @@
 // absolute error, mean absolute error and relative L2 error.
 //
 // stats (float64, device): [0] max |a - b|, [1] sum |a - b|, [2] sum (a - b)^2,
-// [3] sum b^2, [4] element count.  The maximum is exact (non-negative floats
-// compared as integers); the sums are float64 atomics, so their last bits
-// depend on the order the workgroups finish in.
+// [3] sum b^2, [4] element count, and the two figures the pages report, [5]
+// mean |a - b| = [1] / [4] and [6] relative L2 error sqrt([2] / [3]).  The
+// maximum is exact (non-negative floats compared as integers); the sums are
+// float64 atomics, so their last bits depend on the order the workgroups
+// finish in.
 #include "sol_internal.h"
 
 namespace sol {
@@ -20,7 +22,15 @@ namespace {
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
 __global__ __launch_bounds__(64) void gate_clear_kernel(double* __restrict__ stats) {
-    if (threadIdx.x < 5) stats[threadIdx.x] = 0.0;
+    if (threadIdx.x < 7) stats[threadIdx.x] = 0.0;
+}
+
+// mean and relative L2 from the sums (one lane, after gate_kernel)
+__global__ __launch_bounds__(64) void gate_finish_kernel(double* __restrict__ stats) {
+    if (threadIdx.x == 0) {
+        stats[5] = stats[4] > 0.0 ? stats[1] / stats[4] : 0.0;
+        stats[6] = stats[3] > 0.0 ? sqrt(stats[2] / stats[3]) : 0.0;
+    }
 }
 
 // grid: x = row groups of 4 rows, y strides over batch * head; block 256 =
@@ -80,6 +90,9 @@ hipError_t launch_gate(const Geom& g, const void* a, const void* b, double* stat
     dim3 grid((g.N + 3) / 4, min(g.B * g.H, 65535));
     hipLaunchKernelGGL(gate_kernel, grid, dim3(256), 0, stream, (const uint16_t*)a,
                        (const uint16_t*)b, g, stats);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gate_finish_kernel, dim3(1), dim3(64), 0, stream, stats);
     return hipGetLastError();
 }
 

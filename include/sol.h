@@ -199,11 +199,12 @@ sol_status sol_attn_dense_fwd(const void* q, const void* k, const void* v, const
  *                      distinct buffers, neither of them q, k or v (the
  *                      second pass reads the inputs after the first has
  *                      written): SOL_ERR_ARG otherwise.
- *   stats     out, device float64 [5], 8-byte aligned: [0] max |s - d|,
+ *   stats     out, device float64 [7], 8-byte aligned: [0] max |s - d|,
  *             [1] sum |s - d|, [2] sum (s - d)^2, [3] sum d^2, [4] number
- *             of elements compared.  Mean = [1] / [4]; relative L2 =
- *             sqrt([2] / [3]).  The maximum is exact; the sums are float64
- *             atomics whose last bits depend on completion order.
+ *             of elements compared, [5] mean |s - d| = [1] / [4], [6]
+ *             relative L2 error sqrt([2] / [3]) (0 when a divisor is 0).
+ *             The maximum is exact; the sums are float64 atomics whose last
+ *             bits depend on completion order.
  * Other arguments and errors as for sol_attn_fwd.
  */
 sol_status sol_gate_fwd(const void* q, const void* k, const void* v, const sol_desc* desc,
@@ -223,10 +224,8 @@ sol_status sol_gate_fwd(const void* q, const void* k, const void* v, const sol_d
  *
  *   For every valid row x (one head, D channels) at position t of its
  *   sample, with weights gamma (gamma_q for Q, gamma_k for K):
- *     p_c  = fma chain over d = 8c .. 8c+7 ascending of x_d * x_d, from +0
- *            (c = 0 .. D/8 - 1)
- *     ss   = the balanced binary tree of the p_c in index order:
- *            ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)) + ...
+ *     ss   = running float32 sum over d = 0 .. D-1 ascending of x_d * x_d,
+ *            from +0 (each square is exact; one rounding per step)
  *     r    = 1 / sqrt(fma(ss, 1/D, eps))   (each step correctly rounded)
  *     y_d  = (x_d * r) * gamma_d            (per-head RMS normalisation)
  *     RoPE on the channel pairs (2i, 2i+1), with c = cos[t][i], s = sin[t][i]:

@@ -67,3 +67,33 @@ def test_traffic_record_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     stale = dict(rec, attn_src_sha256_16="0" * 16)
     (tmp_path / "traffic.json").write_text(json.dumps(stale))
     assert bench.measured_traffic() is None
+
+
+def test_trace_summary_windows(tmp_path):
+    """--trace-summary: the n-th dispatch of a kernel (in start order) is forward
+    n; the timed window is [warmup, warmup + steps), the cold one follows it."""
+    import csv
+    sys.path.insert(0, ROOT)
+    import bench
+    path = tmp_path / "kt.csv"
+    W, K = 2, 3
+    # attention durations (us): warm-ups 50, 50; timed 10, 12, 14; cold 20, 20, 20
+    attn_us = [50, 50, 10, 12, 14, 20, 20, 20]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 1000
+        # written out of order: the summary sorts by start time
+        rows = []
+        for d in attn_us:
+            rows.append({"Kernel_Name": "attn", "Start_Timestamp": t, "End_Timestamp": t + d * 1000})
+            rows.append({"Kernel_Name": "pool", "Start_Timestamp": t + d * 1000 + 5,
+                         "End_Timestamp": t + d * 1000 + 2005})
+            t += 10 ** 6
+        for r in reversed(rows):
+            w.writerow(r)
+    out = bench.trace_summary(str(path), W, K)
+    a = out["attn"]
+    assert a["calls"] == 8 and a["mean_timed_us"] == 12.0 and a["median_timed_us"] == 12.0
+    assert a["mean_cold_us"] == 20.0 and a["min_us"] == 10.0 and a["max_us"] == 50.0
+    assert out["pool"]["mean_timed_us"] == 2.0
