@@ -17,6 +17,16 @@ from oracle import oracle as orc
 MAX_ABS = 1e-2
 L2_REL = 5e-3
 
+# Tolerance for the optional LSE output (natural log; the pages state none).
+# The kernel weights each key by exp(logit - m) rounded to bf16, the operand
+# its P V product needs, and sums the same rounded weights, so the row sum l
+# carries a relative error of at most 2^-9 (every term positive): ln(1 + 2^-9)
+# = 1.95e-3 in LSE.  On top of that come the float32 logits: 128 exact bf16
+# products summed in float32 miss by at most 127 * 2^-24 * sum |q_d k_d|
+# (about 1.4e-4 nats after the 1/sqrt(128) scale for these inputs), and one
+# rounding each in exp2 and log.  5e-4 covers those three times over.
+LSE_MAX_ABS = math.log1p(2.0 ** -9) + 5e-4
+
 
 def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
     """Half the spacing of bf16 numbers around |x| (8 significant bits)."""
