@@ -424,11 +424,27 @@ hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, fl
                          float tau, int16_t* idx, int32_t* cnt, int64_t* totals,
                          unsigned long long* wg_part, hipStream_t stream)
 {
-    // candidates per lane: up to 4, so each q-bar value read from LDS feeds
-    // up to 4 FMAs; 16 waves x 64 lanes x 4 cover the 4096-candidate limit.
-    // Query blocks per workgroup: 12 with 4 candidates per lane (each k-bar
-    // chunk a lane loads then feeds 12 x 8 x 4 FMAs), 16 otherwise
-    const int jpl = g.ncand <= 64 ? 1 : g.ncand <= 128 ? 2 : 4;
+    // candidates per lane (1, 2, 4 or 5): each q-bar value read from LDS
+    // feeds that many FMAs.  The candidates fill whole waves of 64 lanes, so
+    // the count is chosen to leave the fewest lanes on padding (the score
+    // pass is bound by its VALU FMAs, padded ones included): at 584
+    // candidates 5 per lane fill 2 waves x 320 slots (91%), where 4 per lane
+    // would fill 3 waves x 256 (76%).  Ties go to the larger count.  16 waves
+    // x 64 lanes x 4 cover the 4096-candidate limit.  Query blocks per
+    // workgroup: 12 with 4 or 5 candidates per lane (each k-bar chunk a lane
+    // loads feeds 12 x 8 x JPL FMAs), 16 otherwise.
+    int jpl = 1;
+    if (g.ncand > 64) {
+        long best = -1;
+        for (const int j : {2, 4, 5}) {
+            const long w = (g.ncand + 64 * j - 1) / (64 * j);
+            const long slots = w * 64 * j;
+            if (w <= kMaxWaves && (best < 0 || slots <= best)) {
+                best = slots;
+                jpl = j;
+            }
+        }
+    }
     const int W = (g.ncand + 64 * jpl - 1) / (64 * jpl);
 #define SOL_SELECT_CASE(J, T)                                                               \
     do {                                                                                    \
@@ -442,7 +458,8 @@ hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, fl
     int works = 0;
     if (jpl == 1) SOL_SELECT_CASE(1, 16);
     else if (jpl == 2) SOL_SELECT_CASE(2, 16);
-    else SOL_SELECT_CASE(4, 12);
+    else if (jpl == 4) SOL_SELECT_CASE(4, 12);
+    else SOL_SELECT_CASE(5, 12);
 #undef SOL_SELECT_CASE
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
