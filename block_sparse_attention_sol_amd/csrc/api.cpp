@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "sol.h"
 #include "sol_internal.h"
@@ -221,6 +222,64 @@ sol_status sol_route_pooled(const sol_desc* desc, float tau, int32_t sink_len, f
     return e == hipSuccess ? SOL_OK : SOL_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Static routing scratch of sol_route_noalloc (one copy per GPU, held until
+// the process ends).  In host code `scratch` names a host-side stand-in, not
+// a device address: only the per-device address looked up below is ever
+// passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[SOL_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device
+// with that device current; null on failure.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+sol_status sol_route_noalloc(const void* q, const void* k, const sol_desc* desc, float tau,
+                             int32_t sink_len, float scale, int16_t* blk_idx, int32_t* blk_cnt,
+                             int64_t* totals, int32_t* order, void* stream) {
+    sol::Geom g;
+    const sol_status st = check_desc(desc, sink_len, &g);
+    if (st != SOL_OK) return st;
+    if (q == nullptr || k == nullptr || blk_idx == nullptr || blk_cnt == nullptr || totals == nullptr)
+        return SOL_ERR_ARG;
+    if (std::isnan(tau) || tau < 0.0f || std::isnan(scale) || scale < 0.0f || std::isinf(scale))
+        return SOL_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || (reinterpret_cast<uintptr_t>(totals) & 7u) != 0 ||
+        (reinterpret_cast<uintptr_t>(blk_cnt) & 3u) != 0 || (reinterpret_cast<uintptr_t>(blk_idx) & 1u) != 0 ||
+        (reinterpret_cast<uintptr_t>(order) & 3u) != 0)
+        return SOL_ERR_ALIGN;
+    if (g.NB > 32767 || g.ncand > kMaxCandidates) return SOL_ERR_UNSUPPORTED;
+    // the same figure as sol_route_workspace_bytes (need plus alignment slack)
+    if (sol::route_ws_floats(g) * sizeof(float) + 256 > SOL_NOALLOC_SCRATCH_BYTES) return SOL_ERR_SCRATCH;
+    void* ws = device_scratch();
+    if (ws == nullptr) return SOL_ERR_HIP;
+    const hipError_t e = sol::launch_route(g, q, k, resolve_scale(scale, g.D), tau, blk_idx, blk_cnt,
+                                           totals, order, static_cast<float*>(ws),
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SOL_OK : SOL_ERR_HIP;
+}
+
 const char* sol_status_str(sol_status status) {
     switch (status) {
         case SOL_OK: return "ok";
@@ -229,6 +288,7 @@ const char* sol_status_str(sol_status status) {
         case SOL_ERR_ALIGN: return "misaligned pointer or stride";
         case SOL_ERR_WORKSPACE: return "workspace missing or too small";
         case SOL_ERR_HIP: return "HIP launch failed";
+        case SOL_ERR_SCRATCH: return "call needs more scratch than the static buffer holds";
     }
     return "unknown status";
 }

@@ -18,7 +18,11 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsol.so"
 
 BLOCK = 64
 
-SOL_OK, SOL_ERR_ARG, SOL_ERR_UNSUPPORTED, SOL_ERR_ALIGN, SOL_ERR_WORKSPACE, SOL_ERR_HIP = range(6)
+(SOL_OK, SOL_ERR_ARG, SOL_ERR_UNSUPPORTED, SOL_ERR_ALIGN, SOL_ERR_WORKSPACE, SOL_ERR_HIP,
+ SOL_ERR_SCRATCH) = range(7)
+
+# bytes of the library's static routing scratch (sol_route_noalloc)
+NOALLOC_SCRATCH_BYTES = 48 << 20
 
 
 class SolError(RuntimeError):
@@ -56,6 +60,8 @@ def _load():
     lib.sol_qk_norm_rope_pool.restype = ctypes.c_int
     lib.sol_route_pooled.argtypes = [dp, f32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     lib.sol_route_pooled.restype = ctypes.c_int
+    lib.sol_route_noalloc.argtypes = [vp, vp, dp, f32, i32, f32, vp, vp, vp, vp, vp]
+    lib.sol_route_noalloc.restype = ctypes.c_int
     lib.sol_status_str.argtypes, lib.sol_status_str.restype = [ctypes.c_int], ctypes.c_char_p
     return lib
 
@@ -196,6 +202,25 @@ def route(q: torch.Tensor, k: torch.Tensor, tau: float, sink: int, scale: float 
                        totals.data_ptr(), order.data_ptr() if order is not None else None,
                        workspace.data_ptr(), _nbytes(workspace), _stream(q))
     _check(st, "sol_route")
+    return idx, cnt, totals, order
+
+
+def route_noalloc(q: torch.Tensor, k: torch.Tensor, tau: float, sink: int, scale: float = 0.0,
+                  out=None, cu_seqlens=None, max_seqlen=None):
+    """route() without a workspace: the library's static per-GPU scratch holds the
+    block means (sol_route_noalloc), so with ``out`` given nothing is allocated.
+    Calls that overlap on one GPU race on that scratch.  Same returns as route()."""
+    _check_qkv(q, k)
+    desc = make_desc(q, None, cu_seqlens, max_seqlen)
+    idx, cnt, totals, order = (route_outputs(q, cu_seqlens, max_seqlen) if out is None
+                               else out)
+    _check_lists(q, idx, cnt, order, cu_seqlens, max_seqlen)
+    _check_buffer(totals, torch.int64, (2,), q.device, "totals")
+    st = lib.sol_route_noalloc(q.data_ptr(), k.data_ptr(), ctypes.byref(desc), ctypes.c_float(tau),
+                               int(sink), ctypes.c_float(scale), idx.data_ptr(), cnt.data_ptr(),
+                               totals.data_ptr(),
+                               order.data_ptr() if order is not None else None, _stream(q))
+    _check(st, "sol_route_noalloc")
     return idx, cnt, totals, order
 
 

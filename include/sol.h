@@ -96,7 +96,9 @@ typedef enum {
     SOL_ERR_UNSUPPORTED = 2,  /* D not 64/128, stride along D != 1, a size beyond the limits    */
     SOL_ERR_ALIGN = 3,        /* a pointer or stride that breaks 16-byte row alignment          */
     SOL_ERR_WORKSPACE = 4,    /* workspace null or smaller than sol_route_workspace_bytes()     */
-    SOL_ERR_HIP = 5           /* a kernel launch reported an error                              */
+    SOL_ERR_HIP = 5,          /* a kernel launch reported an error                              */
+    SOL_ERR_SCRATCH = 6       /* sol_route_noalloc: the call needs more scratch than the
+                                 library's static buffer holds (SOL_NOALLOC_SCRATCH_BYTES)     */
 } sol_status;
 
 typedef struct {
@@ -264,6 +266,34 @@ sol_status sol_qk_norm_rope_pool(const void* q, const void* k, const sol_desc* d
 sol_status sol_route_pooled(const sol_desc* desc, float tau, int32_t sink_len, float scale,
                             int16_t* blk_idx, int32_t* blk_cnt, int64_t* totals, int32_t* order,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sol_route_noalloc -- sol_route without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, and harnesses that forbid allocation.  The pooled means and
+ * partial totals that sol_route keeps in the caller's workspace live instead
+ * in a static device array of SOL_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on each GPU it runs on until the process ends.  The call
+ * allocates nothing: no hipMalloc, no hipFree, no allocating library routine.
+ *
+ * Results are identical, bit for bit, to sol_route with a workspace.  A call
+ * whose sol_route_workspace_bytes(desc) exceeds SOL_NOALLOC_SCRATCH_BYTES
+ * returns SOL_ERR_SCRATCH before any launch (the pages' shape
+ * [1, 38247, 56, 128] needs 34.3 MB).  The scratch of the current device is
+ * used, so `stream` must belong to the current device.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (on different
+ * streams or from different threads) race and give unspecified results;
+ * calls ordered on one stream are safe.  No part of the array needs to start
+ * at zero (every call writes what it reads).  The first call on a device
+ * looks up the array's address on that device (hipGetSymbolAddress); a
+ * failure there returns SOL_ERR_HIP.  Other arguments and errors as for
+ * sol_route.
+ */
+#define SOL_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+
+sol_status sol_route_noalloc(const void* q, const void* k, const sol_desc* desc, float tau,
+                             int32_t sink_len, float scale, int16_t* blk_idx, int32_t* blk_cnt,
+                             int64_t* totals, int32_t* order, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* sol_status_str(sol_status status);

@@ -63,7 +63,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert isinstance(lib.status_str(code), str) and lib.status_str(code)
     assert lib.status_str(0) == "ok"
     assert lib.status_str(99) == "unknown status"
@@ -339,3 +339,25 @@ def test_route_pooled_argument_errors(lib):
     assert rp(desc=_desc(lib, N=64 * 5000, H=1)) == 2
     assert lib.lib.sol_route_pooled(None, ctypes.c_float(1.0), 0, ctypes.c_float(0.0), 0x30000,
                                     0x40000, 0x50000, None, 0x60000, 1 << 30, None) == 1
+
+
+@fake_pointers
+def test_route_noalloc_argument_errors(lib):
+    """sol_route_noalloc: sol_route's checks, and a call whose scratch need
+    exceeds the static array is refused (SOL_ERR_SCRATCH) before any launch."""
+    def rn(desc, q=0x10000, k=0x20000, tau=1.0, sink=64, idx=0x30000, cnt=0x40000, tot=0x50000,
+           order=None):
+        return lib.lib.sol_route_noalloc(q, k, ctypes.byref(desc), ctypes.c_float(tau), sink,
+                                         ctypes.c_float(0.0), idx, cnt, tot, order, None)
+    d = _desc(lib)
+    assert rn(d, q=None) == 1
+    assert rn(d, tau=math.nan) == 1
+    assert rn(d, tot=0x50004) == 3
+    assert rn(_desc(lib, D=96)) == 2
+    # the pages' shape fits (34.3 MB); two copies of it (68.7 MB) do not
+    page = _desc(lib, N=38247, H=56)
+    assert lib.lib.sol_route_workspace_bytes(ctypes.byref(page)) <= lib.NOALLOC_SCRATCH_BYTES
+    two = _desc(lib, B=2, N=38247, H=56)
+    assert lib.lib.sol_route_workspace_bytes(ctypes.byref(two)) > lib.NOALLOC_SCRATCH_BYTES
+    assert rn(two, sink=951) == lib.SOL_ERR_SCRATCH == 6
+    assert lib.status_str(6) == "call needs more scratch than the static buffer holds"

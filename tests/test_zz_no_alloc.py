@@ -1,0 +1,71 @@
+"""sol_route_noalloc (routing with the library's static per-GPU scratch instead
+of a caller workspace) against sol_route with a workspace, through the C ABI.
+
+Routing is integer work, so the bar is bit for bit: lists, counts and totals
+equal; the schedule is valid (a permutation with non-increasing counts;
+blocks of equal count may come in any order).  Three calls in a row share the
+one scratch array: the pages' shape (34.3 MB of scratch, near the 48 MiB
+limit), then a smaller and a still smaller call, so each later call runs on
+what the earlier one left behind.  (A call that needs more scratch than the
+array holds is refused on the host; tests/test_abi.py checks that without a
+GPU, so that a regressed check cannot write past the array here.)
+"""
+
+from __future__ import annotations
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import synth
+from tests.helpers import check_schedule, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sol():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import block_sparse_attention_sol_amd as s
+    return s
+
+
+def _same(sol, a, b):
+    import torch
+    idx_a, cnt_a, tot_a, ord_a = a
+    idx_b, cnt_b, tot_b, ord_b = b
+    torch.cuda.synchronize()
+    assert torch.equal(cnt_a, cnt_b) and torch.equal(tot_a, tot_b)
+    mask = torch.arange(idx_a.shape[-1], device=idx_a.device) < cnt_a[..., None]
+    assert torch.equal(torch.where(mask, idx_a, 0), torch.where(mask, idx_b, 0))
+    check_schedule(ord_a.cpu().numpy(), cnt_a.cpu().numpy())
+    check_schedule(ord_b.cpu().numpy(), cnt_b.cpu().numpy())
+
+
+def test_noalloc_equals_route_on_three_calls_in_a_row(sol):
+    import torch
+    page = synth.WORKLOADS["page"]
+    mid = synth.WORKLOADS["mid"]
+    calls = [page, replace(mid, N=3001, H=3), replace(synth.WORKLOADS["tiny"], N=700, H=2)]
+    for w in calls:
+        q_bits, k_bits, _ = synth.make_qkv(w)
+        q, k = to_dev(q_bits), to_dev(k_bits)
+        need = sol.route_workspace_bytes(q)
+        log(f"noalloc {w.name} B={w.B} N={w.N} H={w.H} D={w.D}: workspace {need} bytes")
+        assert need <= sol.NOALLOC_SCRATCH_BYTES
+        # outputs start as garbage, so nothing can pass by being left over
+        out = sol.route_outputs(q)
+        for t in out:
+            t.fill_(-7)
+        got = sol.route_noalloc(q, k, w.tau, w.sink, out=out)
+        ref = sol.route(q, k, w.tau, w.sink)
+        _same(sol, got, ref)
+        # and a second call on the same scratch, with another tau
+        got2 = sol.route_noalloc(q, k, w.tau * 0.5, w.sink)
+        ref2 = sol.route(q, k, w.tau * 0.5, w.sink)
+        _same(sol, got2, ref2)
+        log(f"noalloc {w.name}: equal to sol_route, routed {int(got[2][0].item())} pairs")
+        del q, k
+    torch.cuda.synchronize()
