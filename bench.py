@@ -148,7 +148,8 @@ def trace_summary(csv_path: str, warmup: int, steps: int) -> dict:
     Each forward launches each of its kernels once, so the n-th dispatch of a
     kernel (in start order) belongs to forward n: the first `warmup` are the
     warm-ups, the next `steps` the timed back-to-back forwards of the bench
-    line, and the next `steps` the cold-cache forwards."""
+    line, the next `steps` the cold-cache forwards, and any later dispatches the
+    rest of the run (the separate calls of the packed workload)."""
     import csv
     import statistics
     per = {}
@@ -161,7 +162,10 @@ def trace_summary(csv_path: str, warmup: int, steps: int) -> dict:
         us = [(e - b) / 1e3 for b, e in d]
         warm = us[warmup:warmup + steps]
         cold = us[warmup + steps:warmup + 2 * steps]
+        rest = us[warmup + 2 * steps:]
         out[name] = {"calls": len(us), "mean_all_us": round(statistics.mean(us), 2),
+                     "calls_rest": len(rest),
+                     "mean_rest_us": round(statistics.mean(rest), 2) if rest else None,
                      "mean_timed_us": round(statistics.mean(warm), 2) if warm else None,
                      "median_timed_us": round(statistics.median(warm), 2) if warm else None,
                      "mean_cold_us": round(statistics.mean(cold), 2) if cold else None,
@@ -182,6 +186,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4,
                     help="heads whose whole forward the oracle baseline times")
+    ap.add_argument("--attn-loop", type=float, default=0.0, metavar="SECONDS",
+                    help="only run the attention kernel of the workload (sparse for page, dense "
+                         "for page_dense) back to back for SECONDS, printing 'start' when the "
+                         "loop begins and the mean launch time at the end: a steady load for "
+                         "reading the board's power and clock sensors")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="per-kernel durations (all, timed window, cold window) from a rocprofv3 "
                          "kernel-trace CSV of a bench run with the same --warmup/--steps; no GPU")
@@ -285,6 +294,25 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    if args.attn_loop > 0:
+        def attn_only():
+            if dense:
+                sol.attn_dense(q, k, v, out=o, **vk)
+            else:
+                sol.attn(qa, ka, v, idx, cnt, w.sink, out=o, order=order, **vk)
+        err("start")
+        t_loop0 = time.perf_counter()
+        launches = 0
+        while time.perf_counter() - t_loop0 < args.attn_loop:
+            for _ in range(4):
+                attn_only()
+            torch.cuda.synchronize()
+            launches += 4
+        dt = time.perf_counter() - t_loop0
+        err(f"{args.workload} attention loop: {launches} launches in {dt:.2f} s, "
+            f"{dt / launches * 1e3:.3f} ms per launch")
+        return 0
 
     # per-kernel events on the stream the kernels run on (torch's current stream)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
