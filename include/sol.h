@@ -42,7 +42,9 @@
  *
  * Conventions for every entry point:
  *   - Tensors are device pointers owned by the caller; the library never
- *     allocates or frees memory and keeps no per-call state.
+ *     allocates or frees memory and keeps no per-call state.  (The one
+ *     exception to the second part is sol_route_noalloc, whose scratch is a
+ *     static device array per GPU; see there.)
  *   - Q, K, V are [B, N, H, D] bf16 with element strides (sb, sn, sh) shared
  *     by the three tensors (they may be views of one merged QKV projection)
  *     and unit stride along D; O has its own strides.  Rows >= N are never
@@ -74,8 +76,11 @@
  *     device state.  SOL_ERR_HIP means a kernel launch failed.
  *   - D must be 64 or 128.  Base pointers and strides must give 16-byte
  *     aligned rows.
- *   - Thread safety: calls on different streams may run concurrently; the
- *     library has no mutable global state.
+ *   - Thread safety: calls on different streams may run concurrently.  The
+ *     only mutable global state is sol_route_noalloc's static scratch array
+ *     on each GPU and the cache of its per-device address (filled under a
+ *     mutex): overlapping sol_route_noalloc calls on one GPU race on that
+ *     array; every other entry point works only on the caller's buffers.
  */
 #ifndef SOL_H
 #define SOL_H
