@@ -142,6 +142,29 @@ def cpu_baseline(w, q_bits, k_bits, v_bits, n_heads: int):
     }
 
 
+def block_pairs(cnt, first, lengths, sink: int) -> int:
+    """Block pairs (i, j) that hold at least one attended key, sink or routed,
+    summed over the batch and heads: the 64 x 64 tiles the attention kernel
+    computes.  Every query block of sample b sees its sink blocks
+    ceil(min(S, n_b) / 64), plus its listed blocks, except that a listed
+    straddle block (the block holding key S when S is not a multiple of 64)
+    is already one of the sink blocks.  cnt and first are the routing counts
+    and the first list entries, [B, H, NB] each; lengths the sample lengths."""
+    import numpy as np
+    cnt = np.asarray(cnt, np.int64)
+    first = np.asarray(first, np.int64)
+    H = cnt.shape[1]
+    total = 0
+    for b, n in enumerate(lengths):
+        nb = (n + 63) // 64
+        nsink = (min(sink, n) + 63) // 64
+        c = cnt[b, :, :nb]
+        total += H * nb * nsink + int(c.sum())
+        if sink % 64 and sink < n:
+            total -= int(((c > 0) & (first[b, :, :nb] == sink // 64)).sum())
+    return total
+
+
 def trace_summary(csv_path: str, warmup: int, steps: int) -> dict:
     """Per-kernel durations from a rocprofv3 --kernel-trace CSV of one bench run.
 
@@ -402,15 +425,7 @@ def main() -> int:
     if dense:
         tile_pairs = H * sum(nb * nb for nb in nbs)
     else:
-        first = idx[..., 0].cpu().numpy().astype(np.int64)
-        c = cnt.cpu().numpy().astype(np.int64)
-        straddles = 0
-        if w.sink % 64:
-            for bb, (n, nb) in enumerate(zip(lengths, nbs)):
-                if w.sink < n:
-                    straddles += int(((c[bb, :, :nb] > 0) & (first[bb, :, :nb] == w.sink // 64)).sum())
-        nsink_tiles = [(min(w.sink, n) + 63) // 64 for n in lengths]
-        tile_pairs = H * sum(nb * ns for nb, ns in zip(nbs, nsink_tiles)) + routed - straddles
+        tile_pairs = block_pairs(cnt.cpu().numpy(), idx[..., 0].cpu().numpy(), lengths, w.sink)
     flop_tile = 4.0 * D * 64 * 64 * tile_pairs
     rho_route = routed / cand_pairs
     rho_pair = pairs / (H * sum(n * n for n in lengths))

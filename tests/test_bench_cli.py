@@ -97,3 +97,40 @@ def test_trace_summary_windows(tmp_path):
     assert a["calls"] == 8 and a["mean_timed_us"] == 12.0 and a["median_timed_us"] == 12.0
     assert a["mean_cold_us"] == 20.0 and a["min_us"] == 10.0 and a["max_us"] == 50.0
     assert out["pool"]["mean_timed_us"] == 2.0
+
+
+def test_block_pairs_match_the_oracles_block_density():
+    """The bench's exact block-density numerator equals the oracle's count of
+    block pairs with an attended key, on routed cases with and without a
+    straddle block, an empty sink, a sink as long as the sequence, and a
+    batch of unequal lengths."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    from oracle import oracle as orc
+    for N, S, tau, seed in [(1000, 951, 0.4, 1), (700, 0, 0.3, 2), (640, 128, 0.2, 3),
+                            (300, 300, 1.0, 4), (2000, 95, 0.0, 5), (130, 63, 10.0, 6)]:
+        rng = np.random.default_rng(seed)
+        q = rng.standard_normal((1, N, 3, 64)).astype(np.float32)
+        k = rng.standard_normal((1, N, 3, 64)).astype(np.float32)
+        r = orc.route(q, k, N, S, tau)
+        NB = r.geom.NB
+        first = np.where(r.sel.any(-1), r.sel.argmax(-1), -1)
+        got = bench.block_pairs(r.cnt, first, [N], S)
+        assert got == orc.densities(r, 1, 3)["block"][0], (N, S, tau)
+    # a batch of samples of unequal lengths, padded to the longest
+    lengths, S, H = [500, 64, 1000], 96, 2
+    NBmax = (max(lengths) + 63) // 64
+    cnt = np.zeros((3, H, NBmax), np.int64)
+    first = np.full((3, H, NBmax), -1, np.int64)
+    want = 0
+    for b, n in enumerate(lengths):
+        rng = np.random.default_rng(10 + b)
+        q = rng.standard_normal((1, n, H, 64)).astype(np.float32)
+        k = rng.standard_normal((1, n, H, 64)).astype(np.float32)
+        r = orc.route(q, k, n, S, 0.3)
+        nb = r.geom.NB
+        cnt[b, :, :nb] = r.cnt[0]
+        first[b, :, :nb] = np.where(r.sel[0].any(-1), r.sel[0].argmax(-1), -1)
+        want += orc.densities(r, 1, H)["block"][0]
+    assert bench.block_pairs(cnt, first, lengths, S) == want
