@@ -165,6 +165,36 @@ def block_pairs(cnt, first, lengths, sink: int) -> int:
     return total
 
 
+def locality_lists(cnt, nb: int, j0: int, kind: str, seed: int = 5):
+    """Routed lists with the same per-block counts as cnt ([B, H, NB] int, on the
+    host) but another key locality, as int16 [B, H, NB, nb] on the host: row
+    (b, h, i) holds cnt[b, h, i] ascending candidates of [j0, nb).  "prefix"
+    gives every row the first candidates j0, j0 + 1, ... (every walk touches
+    the same tiles: the most L2 reuse any schedule could get); "random" a
+    seeded uniform subset (no structure at all).  They are valid inputs of the
+    attention kernel with its work per block unchanged, for measuring what
+    the key locality of the routed lists costs."""
+    import torch
+    B, H, nbr = cnt.shape
+    ncand = nb - j0
+    rows = B * H * nbr
+    c = cnt.reshape(rows, 1).to(torch.int64)
+    if int(c.min()) < 0 or int(c.max()) > ncand:
+        raise ValueError("counts must lie in [0, NB - j0]")
+    keep = torch.arange(ncand)[None, :] < c
+    if kind == "prefix":
+        vals = j0 + torch.arange(ncand)[None, :].expand(rows, ncand)
+    elif kind == "random":
+        g = torch.Generator().manual_seed(seed)
+        perm = torch.rand(rows, ncand, generator=g).argsort(dim=1)
+        vals = torch.where(keep, perm, torch.full_like(perm, ncand)).sort(dim=1).values + j0
+    else:
+        raise ValueError(f"unknown list kind {kind!r}")
+    out = torch.zeros(rows, nb, dtype=torch.int16)
+    out[:, :ncand] = torch.where(keep, vals, torch.zeros_like(vals)).to(torch.int16)
+    return out.reshape(B, H, nbr, nb)
+
+
 def trace_summary(csv_path: str, warmup: int, steps: int) -> dict:
     """Per-kernel durations from a rocprofv3 --kernel-trace CSV of one bench run.
 
@@ -196,6 +226,79 @@ def trace_summary(csv_path: str, warmup: int, steps: int) -> dict:
     return out
 
 
+def _median_ms(fn, reps: int):
+    import torch
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        ev0.record()
+        fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        ts.append(ev0.elapsed_time(ev1))
+    ts.sort()
+    return {"median_ms": round(ts[len(ts) // 2], 4), "min_ms": round(ts[0], 4),
+            "max_ms": round(ts[-1], 4)}
+
+
+def list_locality(args, sol, w, q, k, v, o, idx, cnt, order) -> int:
+    """The attention kernel on list sets of equal counts and different key
+    locality (locality_lists), round robin, --steps launches each."""
+    import torch
+    kinds = args.list_locality.split(",")
+    B, H, NB, _ = idx.shape
+    j0 = w.sink // 64 if w.sink < w.N else NB
+    cnt_h = cnt.cpu()
+    sets = {}
+    for kind in kinds:
+        if kind == "routed":
+            sets[kind] = idx
+        else:
+            sets[kind] = locality_lists(cnt_h, NB, j0, kind).to(q.device)
+    times = {kind: [] for kind in kinds}
+    for kind in kinds:
+        sol.attn(q, k, v, sets[kind], cnt, w.sink, out=o, order=order)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        for kind in kinds:
+            times[kind].append(_median_ms(
+                lambda: sol.attn(q, k, v, sets[kind], cnt, w.sink, out=o, order=order), 1)["median_ms"])
+    rec = {"list_locality": {kind: {"median_ms": round(sorted(t)[len(t) // 2], 4),
+                                    "min_ms": round(min(t), 4), "max_ms": round(max(t), 4)}
+                             for kind, t in times.items()},
+           "launches_each": args.steps, "schedule": "routing order (longest list first)",
+           "workload": f"[{w.B},{w.N},{w.H},{w.D}] bf16, sink {w.sink}, tau {w.tau}"}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def platform_flash(args, sol, q, k, v, o) -> int:
+    """torch's scaled_dot_product_attention restricted to its flash backend
+    (an unavailable backend raises instead of falling back to the math path)
+    against sol_attn_dense_fwd on the same inputs."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    B, N, H, D = q.shape
+    flop = 4.0 * B * H * N * N * D
+    ours = _median_ms(lambda: sol.attn_dense(q, k, v, out=o), max(args.steps, 3))
+    rec = {"ours_dense": {**ours, "tflops": round(flop / ours["median_ms"] / 1e9, 1)}}
+    qt, kt, vt = (x.permute(0, 2, 1, 3).contiguous() for x in (q, k, v))
+    try:
+        rec["torch_fa_library"] = str(torch.backends.cuda.preferred_rocm_fa_library())
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            ot = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)
+            torch.cuda.synchronize()
+            t = _median_ms(lambda: torch.nn.functional.scaled_dot_product_attention(qt, kt, vt),
+                           max(args.steps, 3))
+        rec["torch_flash"] = {**t, "tflops": round(flop / t["median_ms"] / 1e9, 1)}
+        rec["max_abs_diff"] = float((ot.permute(0, 2, 1, 3).float() - o.float()).abs().max())
+    except RuntimeError as e:
+        rec["torch_flash"] = f"unavailable: {str(e)[:200]}"
+    rec["workload"] = f"dense [{B},{N},{H},{D}] bf16"
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,6 +317,16 @@ def main() -> int:
                          "for page_dense) back to back for SECONDS, printing 'start' when the "
                          "loop begins and the mean launch time at the end: a steady load for "
                          "reading the board's power and clock sensors")
+    ap.add_argument("--list-locality", metavar="KINDS",
+                    help="page workload only: time the attention kernel --steps times on each "
+                         "of the comma-separated list sets routed, prefix and random (same "
+                         "counts per block, different key locality), print one JSON object "
+                         "and exit")
+    ap.add_argument("--platform-flash", action="store_true",
+                    help="page_dense workload only: time torch's own flash attention "
+                         "(scaled_dot_product_attention, flash backend only) against this "
+                         "library's dense kernel on the same inputs, print one JSON object "
+                         "and exit")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="per-kernel durations (all, timed window, cold window) from a rocprofv3 "
                          "kernel-trace CSV of a bench run with the same --warmup/--steps; no GPU")
@@ -317,6 +430,17 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    if args.list_locality:
+        if args.workload != "page":
+            err("--list-locality needs --workload page")
+            return 2
+        return list_locality(args, sol, w, q, k, v, o, idx, cnt, order)
+    if args.platform_flash:
+        if args.workload != "page_dense":
+            err("--platform-flash needs --workload page_dense")
+            return 2
+        return platform_flash(args, sol, q, k, v, o)
 
     if args.attn_loop > 0:
         def attn_only():

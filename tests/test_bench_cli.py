@@ -134,3 +134,40 @@ def test_block_pairs_match_the_oracles_block_density():
         first[b, :, :nb] = np.where(r.sel[0].any(-1), r.sel[0].argmax(-1), -1)
         want += orc.densities(r, 1, H)["block"][0]
     assert bench.block_pairs(cnt, first, lengths, S) == want
+
+
+def test_locality_lists_are_valid_and_keep_the_counts():
+    """The list sets of the locality measurement are valid attention inputs
+    with the routed counts: every row holds cnt ascending candidates of
+    [j0, NB); "prefix" rows are j0, j0 + 1, ...; "random" rows are a seeded
+    draw (the same seed gives the same lists, another seed other lists)."""
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    B, H, NB, j0 = 2, 3, 40, 14
+    g = torch.Generator().manual_seed(0)
+    cnt = torch.randint(0, NB - j0 + 1, (B, H, NB), generator=g, dtype=torch.int32)
+    cnt[0, 0, 0], cnt[0, 0, 1] = 0, NB - j0          # the empty and the full list
+    for kind in ("prefix", "random"):
+        L = bench.locality_lists(cnt, NB, j0, kind)
+        assert L.dtype == torch.int16 and tuple(L.shape) == (B, H, NB, NB)
+        for b in range(B):
+            for h in range(H):
+                for i in range(NB):
+                    c = int(cnt[b, h, i])
+                    row = L[b, h, i, :c].to(torch.int64)
+                    assert row.numel() == c
+                    if c:
+                        assert int(row.min()) >= j0 and int(row.max()) < NB
+                        assert bool((row[1:] > row[:-1]).all())
+                    if kind == "prefix":
+                        assert torch.equal(row, torch.arange(j0, j0 + c))
+    assert torch.equal(bench.locality_lists(cnt, NB, j0, "random"),
+                       bench.locality_lists(cnt, NB, j0, "random"))
+    assert not torch.equal(bench.locality_lists(cnt, NB, j0, "random", seed=1),
+                           bench.locality_lists(cnt, NB, j0, "random", seed=2))
+    try:
+        bench.locality_lists(cnt + NB, NB, j0, "prefix")
+        raise AssertionError("counts above NB - j0 must be refused")
+    except ValueError:
+        pass
