@@ -299,6 +299,31 @@ def platform_flash(args, sol, q, k, v, o) -> int:
     return 0
 
 
+def gemm_peak(args) -> int:
+    """Measured dense bf16 contraction rate of this chip: torch.matmul on square,
+    contiguous, seeded operands (float32 accumulation inside the library), the
+    median of --steps launches after warm-up, at three sizes."""
+    import torch
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    rec = {"gemm_bf16": {}}
+    for n in (4096, 8192, 16384):
+        a = torch.randn(n, n, device="cuda:0", generator=g).to(torch.bfloat16)
+        b = torch.randn(n, n, device="cuda:0", generator=g).to(torch.bfloat16)
+        c = torch.empty(n, n, device="cuda:0", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        t = _median_ms(lambda: torch.matmul(a, b, out=c), max(args.steps, 5))
+        tf = 2.0 * n ** 3 / t["median_ms"] / 1e9
+        rec["gemm_bf16"][str(n)] = {**t, "tflops": round(tf, 1),
+                                    "frac_of_spec": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del a, b, c
+    rec["spec_peak_tflops"] = PEAK_BF16_TFLOPS
+    rec["library"] = "torch.matmul (hipBLASLt / rocBLAS), bf16 in and out"
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,6 +352,11 @@ def main() -> int:
                          "(scaled_dot_product_attention, flash backend only) against this "
                          "library's dense kernel on the same inputs, print one JSON object "
                          "and exit")
+    ap.add_argument("--gemm-peak", action="store_true",
+                    help="time torch's bf16 matrix product (the platform's GEMM library) on "
+                         "square contiguous operands of 4096, 8192 and 16384, print one JSON "
+                         "object with the measured dense bf16 MFMA rate and exit (context for "
+                         "the spec peak the roofline uses)")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="per-kernel durations (all, timed window, cold window) from a rocprofv3 "
                          "kernel-trace CSV of a bench run with the same --warmup/--steps; no GPU")
@@ -366,6 +396,9 @@ def main() -> int:
         torch.cuda.synchronize()
         err(f"copied {args.copy_calibration} bytes 5 times")
         return 0
+
+    if args.gemm_peak:
+        return gemm_peak(args)
 
     import block_sparse_attention_sol_amd as sol
     import synth
