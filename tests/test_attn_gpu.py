@@ -94,12 +94,24 @@ def page_inputs():
 
 def test_attention_parity_page_shape_all_blocks_of_four_heads(sol, page_inputs):
     """Every query block (598 each, the ragged last one and the sink straddle
-    block included) of four of the 56 heads, after a bit-exact comparison of
-    the whole routing mask."""
+    block included) of four of the 56 heads, and in every other head the
+    first, the straddle (14), the first fully routable (15) and the last
+    block plus four seeded others, after a bit-exact comparison of the whole
+    routing mask."""
     w = synth.WORKLOADS["page"]
     g = orc.geometry(w.N, w.sink)
     blocks = [(0, h, i) for h in PAGE_HEADS for i in range(g.NB)]
-    log(f"attention parity page, all {len(blocks)} query blocks of heads {PAGE_HEADS}")
+    rng = np.random.default_rng(56)
+    fixed = {0, g.S // 64, g.S // 64 + 1, g.NB - 1}
+    for h in range(w.H):
+        if h in PAGE_HEADS:
+            continue
+        pick = set(fixed)
+        while len(pick) < 8:
+            pick.add(int(rng.integers(g.NB)))
+        blocks += [(0, h, i) for i in sorted(pick)]
+    log(f"attention parity page, all query blocks of heads {PAGE_HEADS} and 8 of each "
+        f"other head: {len(blocks)} blocks")
     _run(sol, w, blocks=blocks, inputs=page_inputs)
 
 
