@@ -9,13 +9,17 @@
 // always kept) and its exact float32 order are stated in include/sol.h.
 //
 // Two kernels:
-//   pool_kernel          HBM-bound scan of Q and K (each element read once);
-//                        one lane owns 8 channels of one head and adds the
-//                        block's rows in ascending order.
+//   pool_kernel          HBM-bound scan of K (and of Q when routing from
+//                        means is not fused, see below; each element read
+//                        once); one lane owns 8 channels of one head and adds
+//                        the block's rows in ascending order.
 //   score_select_kernel  one lane owns one candidate key block (or a few) and
-//                        the workgroup's 16 query blocks, whose pooled rows
-//                        sit in LDS; the channels go in 8-wide chunks; each
-//                        score is an FMA chain over d ascending.
+//                        the workgroup's 12 or 16 query blocks, whose pooled
+//                        rows sit in LDS; the channels go in 8-wide chunks;
+//                        each score is an FMA chain over d ascending.  In
+//                        sol_route the workgroup pools its query blocks from
+//                        Q itself (the same order as pool_kernel), so the scan
+//                        of Q overlaps other workgroups' scoring.
 #include "sol_internal.h"
 
 namespace sol {
@@ -40,16 +44,17 @@ __device__ __forceinline__ void add8(float (&acc)[8], const uint4& w) {
     acc[6] += bf_lo(w.w); acc[7] += bf_hi(w.w);
 }
 
-// grid: x = token block, y = lane groups of 256 over H * D / 8, z = batch * 2 + (0: Q, 1: K)
+// grid: x = token block, y = lane groups of 256 over H * D / 8, z = batch * 2 + (0: Q, 1: K),
+// or z = batch with k_only (the Q means are then pooled by the scoring kernel)
 // qbar: [B, H, NB, D] float32; kbar: [B, H, D / 8, NB, 8] float32 (8-channel
 // chunks, so a lane owning one key block reads its chunk contiguously).
 __global__ __launch_bounds__(256) void pool_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom g,
-    float* __restrict__ qbar, float* __restrict__ kbar)
+    float* __restrict__ qbar, float* __restrict__ kbar, int k_only)
 {
     const int blk = blockIdx.x;
-    const int b = blockIdx.z >> 1;
-    const int is_k = blockIdx.z & 1;
+    const int b = k_only ? (int)blockIdx.z : (int)(blockIdx.z >> 1);
+    const int is_k = k_only ? 1 : (int)(blockIdx.z & 1);
     const int chunks = g.D >> 3;
     const int lane_id = blockIdx.y * 256 + threadIdx.x;
     if (lane_id >= g.H * chunks) return;
@@ -132,13 +137,21 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 constexpr int kMaxWaves = 16;
 
+// query blocks per scoring workgroup when it pools them itself
+#ifndef SOL_POOLQ_TI
+#define SOL_POOLQ_TI 12
+#endif
+
 // grid: x = query-block tiles of TI (XCD-remapped together with y), y = B * H
 // block: 64 * W threads; lane slot s = jj * 64 W + tid owns candidate j = j0 + s.
-template <int D, int JPL, int TI>
+// POOLQ: the workgroup pools its own TI query blocks from q (same order and
+// arithmetic as pool_kernel) instead of reading q-bar, so the HBM-bound scan
+// of Q runs in workgroups that overlap the VALU-bound scoring of others.
+template <int D, int JPL, int TI, bool POOLQ>
 __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ kbar, Geom g, float scale,
-    float tau, int tiles_per_bh, int16_t* __restrict__ idx, int32_t* __restrict__ cnt,
-    unsigned long long* __restrict__ wg_part)
+    const float* __restrict__ qbar, const uint16_t* __restrict__ q, const float* __restrict__ kbar,
+    Geom g, float scale, float tau, int tiles_per_bh, int16_t* __restrict__ idx,
+    int32_t* __restrict__ cnt, unsigned long long* __restrict__ wg_part)
 {
     const int work = xcd_remap(blockIdx.x, gridDim.x, tiles_per_bh * g.B * g.H);
     if (work < 0) return;
@@ -180,9 +193,40 @@ __global__ __launch_bounds__(64 * kMaxWaves) void score_select_kernel(
         wg_tot[0] = 0;
         wg_tot[1] = 0;
     }
-    for (int e = tid; e < TI * D; e += blockDim.x) {
-        const int ii = e / D;
-        qs[ii][e - ii * D] = ii < ni ? qb[(int64_t)(i0 + ii) * D + (e - ii * D)] : 0.f;
+    if constexpr (POOLQ) {
+        // one (query block, 8-channel chunk) per lane and pass: the block's
+        // valid rows added in ascending order, loads issued 16 ahead, one
+        // divide -- the q-bar of pool_kernel, bit for bit
+        constexpr int CH = D / 8;
+        const uint16_t* qsrc = q + sq.base + (int64_t)(bh % g.H) * g.sh;
+        for (int e = tid; e < TI * CH; e += blockDim.x) {
+            const int ii = e / CH, c = e - ii * CH;
+            float a8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            float rows = 1.f;
+            if (ii < ni) {
+                const int r0 = (i0 + ii) * kBlock;
+                const int r1 = min(r0 + kBlock, sq.N);
+                const uint16_t* src = qsrc + c * 8;
+                int t = r0;
+                for (; t + 16 <= r1; t += 16) {
+                    uint4 w[16];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+                        w[u] = load_stream16(src + (int64_t)(t + u) * g.sn);
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) add8(a8, w[u]);
+                }
+                for (; t < r1; ++t) add8(a8, load_stream16(src + (int64_t)t * g.sn));
+                rows = (float)(r1 - r0);
+            }
+#pragma unroll
+            for (int x = 0; x < 8; ++x) qs[ii][8 * c + x] = a8[x] / rows;
+        }
+    } else {
+        for (int e = tid; e < TI * D; e += blockDim.x) {
+            const int ii = e / D;
+            qs[ii][e - ii * D] = ii < ni ? qb[(int64_t)(i0 + ii) * D + (e - ii * D)] : 0.f;
+        }
     }
     __syncthreads();
     int jrow[JPL];
@@ -420,8 +464,8 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
 }
 
 template <int D>
-hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, float scale,
-                         float tau, int16_t* idx, int32_t* cnt, int64_t* totals,
+hipError_t launch_select(const Geom& g, const float* qbar, const uint16_t* q, const float* kbar,
+                         float scale, float tau, int16_t* idx, int32_t* cnt, int64_t* totals,
                          unsigned long long* wg_part, hipStream_t stream)
 {
     // candidates per lane (1, 2, 4 or 5): each q-bar value read from LDS
@@ -446,20 +490,28 @@ hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, fl
         }
     }
     const int W = (g.ncand + 64 * jpl - 1) / (64 * jpl);
-#define SOL_SELECT_CASE(J, T)                                                               \
+#define SOL_SELECT_CASE(J, T, P)                                                            \
     do {                                                                                    \
         const int tiles = (g.NB + (T) - 1) / (T);                                           \
         const int total = tiles * g.B * g.H;                                                \
         const int grid = round_up(total, kXcds);                                            \
-        hipLaunchKernelGGL((score_select_kernel<D, J, T>), dim3(grid), dim3(64 * W), 0,     \
-                           stream, qbar, kbar, g, scale, tau, tiles, idx, cnt, wg_part);    \
+        hipLaunchKernelGGL((score_select_kernel<D, J, T, P>), dim3(grid), dim3(64 * W), 0,  \
+                           stream, qbar, q, kbar, g, scale, tau, tiles, idx, cnt, wg_part); \
         works = total;                                                                      \
     } while (0)
     int works = 0;
-    if (jpl == 1) SOL_SELECT_CASE(1, 16);
-    else if (jpl == 2) SOL_SELECT_CASE(2, 16);
-    else if (jpl == 4) SOL_SELECT_CASE(4, 12);
-    else SOL_SELECT_CASE(5, 12);
+    if (q != nullptr) {
+        // pooling its own query blocks: SOL_POOLQ_TI of them per workgroup
+        if (jpl == 1) SOL_SELECT_CASE(1, SOL_POOLQ_TI, true);
+        else if (jpl == 2) SOL_SELECT_CASE(2, SOL_POOLQ_TI, true);
+        else if (jpl == 4) SOL_SELECT_CASE(4, SOL_POOLQ_TI, true);
+        else SOL_SELECT_CASE(5, SOL_POOLQ_TI, true);
+    } else {
+        if (jpl == 1) SOL_SELECT_CASE(1, 16, false);
+        else if (jpl == 2) SOL_SELECT_CASE(2, 16, false);
+        else if (jpl == 4) SOL_SELECT_CASE(4, 12, false);
+        else SOL_SELECT_CASE(5, 12, false);
+    }
 #undef SOL_SELECT_CASE
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -468,13 +520,14 @@ hipError_t launch_select(const Geom& g, const float* qbar, const float* kbar, fl
 }
 
 // scores and selection from the block means, then the schedule
-hipError_t select_and_order(const Geom& g, const float* qbar, const float* kbar, float scale,
-                            float tau, int16_t* idx, int32_t* cnt, int64_t* totals,
-                            int32_t* order, unsigned long long* wg_part, hipStream_t stream)
+hipError_t select_and_order(const Geom& g, const float* qbar, const uint16_t* q,
+                            const float* kbar, float scale, float tau, int16_t* idx, int32_t* cnt,
+                            int64_t* totals, int32_t* order, unsigned long long* wg_part,
+                            hipStream_t stream)
 {
     hipError_t e = g.D == 128
-        ? launch_select<128>(g, qbar, kbar, scale, tau, idx, cnt, totals, wg_part, stream)
-        : launch_select<64>(g, qbar, kbar, scale, tau, idx, cnt, totals, wg_part, stream);
+        ? launch_select<128>(g, qbar, q, kbar, scale, tau, idx, cnt, totals, wg_part, stream)
+        : launch_select<64>(g, qbar, q, kbar, scale, tau, idx, cnt, totals, wg_part, stream);
     if (e != hipSuccess || order == nullptr) return e;
     hipLaunchKernelGGL(order_kernel, dim3(g.B * g.H), dim3(256), (size_t)(g.ncand + 1) * sizeof(int),
                        stream, cnt, g, order);
@@ -484,9 +537,10 @@ hipError_t select_and_order(const Geom& g, const float* qbar, const float* kbar,
 }  // namespace
 
 // partial totals of the scoring workgroups: two uint64 per workgroup, at most
-// ceil(NB / 12) workgroups per (batch, head)
+// ceil(NB / min tile) workgroups per (batch, head)
 static size_t part_floats(const Geom& g) {
-    const size_t works = (size_t)((g.NB + 11) / 12) * g.B * g.H;
+    constexpr int kMinTile = SOL_POOLQ_TI < 12 ? SOL_POOLQ_TI : 12;
+    const size_t works = (size_t)((g.NB + kMinTile - 1) / kMinTile) * g.B * g.H;
     return (4 * works + 63) / 64 * 64;
 }
 
@@ -511,12 +565,13 @@ hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale
     float* qbar = ws;
     float* kbar = ws + one;
     const int lanes = g.H * (g.D / 8);
-    dim3 grid(g.NB, (lanes + 255) / 256, g.B * 2);
+    // the K means here; the scoring workgroups pool their own query blocks
+    dim3 grid(g.NB, (lanes + 255) / 256, g.B);
     hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, stream, (const uint16_t*)q,
-                       (const uint16_t*)k, g, qbar, kbar);
+                       (const uint16_t*)k, g, qbar, kbar, 1);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return select_and_order(g, qbar, kbar, scale, tau, idx, cnt, totals, order,
+    return select_and_order(g, qbar, (const uint16_t*)q, kbar, scale, tau, idx, cnt, totals, order,
                             reinterpret_cast<unsigned long long*>(ws + 2 * one), stream);
 }
 
@@ -530,7 +585,7 @@ hipError_t launch_route_pooled(const Geom& g, float scale, float tau, int16_t* i
         return hipGetLastError();
     }
     const size_t one = ((size_t)g.B * g.H * g.NB * g.D + 63) / 64 * 64;
-    return select_and_order(g, ws, ws + one, scale, tau, idx, cnt, totals, order,
+    return select_and_order(g, ws, nullptr, ws + one, scale, tau, idx, cnt, totals, order,
                             reinterpret_cast<unsigned long long*>(ws + 2 * one), stream);
 }
 

@@ -118,9 +118,11 @@ typedef struct {
 /* Number of 64-token blocks, ceil(N / 64) (0 for N <= 0). */
 int32_t sol_num_blocks(int32_t N);
 
-/* Device workspace that sol_route needs, in bytes: the pooled queries and
- * keys, 2 * B * H * NB * D float32, then scratch for the partial totals of
- * the scoring pass (16 bytes per 12 query blocks per (batch, head)), plus
+/* Device workspace that sol_route needs, in bytes: room for the pooled
+ * queries and keys, 2 * B * H * NB * D float32 (sol_qk_norm_rope_pool writes
+ * both there; sol_route itself stores only the key means, its scoring pass
+ * pools the queries on chip), then scratch for the partial totals of the
+ * scoring pass (16 bytes per 12 query blocks per (batch, head)), plus
  * alignment.  0 for an invalid desc. */
 size_t sol_route_workspace_bytes(const sol_desc* desc);
 
