@@ -299,6 +299,56 @@ def platform_flash(args, sol, q, k, v, o) -> int:
     return 0
 
 
+def varlen_calls(args, sol, synth) -> int:
+    """One forward (routing + attention) per variable-length prompt, each on its
+    own fixed-length call of the one ahead-of-time build; per call the median
+    and best of --steps timed forwards after one untimed forward (the first
+    call's first forward is reported too: no compile happens at a new length)."""
+    import numpy as np
+    import torch
+    calls = synth.varlen_calls()
+    rows, first_ms = [], None
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for n, w in enumerate(calls):
+        q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+                   for x in synth.make_qkv(w))
+        o = torch.empty_like(q)
+        ws = torch.empty(max(sol.route_workspace_bytes(q), 256), dtype=torch.uint8, device=q.device)
+        outs = sol.route_outputs(q)
+        ts = []
+        for rep in range(args.steps + 1):
+            ev0.record()
+            sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs)
+            sol.attn(q, k, v, outs[0], outs[1], w.sink, out=o, order=outs[3])
+            ev1.record()
+            torch.cuda.synchronize()
+            t = ev0.elapsed_time(ev1)
+            if n == 0 and rep == 0:
+                first_ms = t
+            if rep > 0:
+                ts.append(t)
+        tot = outs[2].cpu().numpy()
+        nb = sol.num_blocks(w.N)
+        ncand = nb - (nb if w.sink >= w.N else w.sink // 64)
+        flop = 4.0 * w.D * int(tot[1])
+        med, best = float(np.median(ts)), float(min(ts))
+        rows.append({"N": w.N, "median_ms": round(med, 4), "best_ms": round(best, 4),
+                     "tflops_median": round(flop / med / 1e9, 1),
+                     "route_density": round(int(tot[0]) / (w.B * w.H * nb * ncand), 6),
+                     "effective_flop": flop})
+        err(f"{w.name}: N={w.N} median {med:.3f} ms, best {best:.3f} ms, "
+            f"{flop / med / 1e9:.1f} TFLOP/s")
+        del q, k, v, o, ws, outs
+    per_flop = [r["median_ms"] / r["effective_flop"] for r in rows]
+    rec = {"varlen_calls": rows, "steps_each": args.steps,
+           "worst_over_median_ms_per_flop": round(max(per_flop) / float(np.median(per_flop)), 4),
+           "first_forward_ms": round(first_ms, 3),
+           "workload": f"16 prompts, N in [36000, 40000] from the seeded draw, H {calls[0].H}, "
+                       f"D {calls[0].D}, sink {calls[0].sink}, tau {calls[0].tau}, bf16"}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def gemm_peak(args) -> int:
     """Measured dense bf16 contraction rate of this chip: torch.matmul on square,
     contiguous, seeded operands (float32 accumulation inside the library), the
@@ -357,6 +407,11 @@ def main() -> int:
                          "square contiguous operands of 4096, 8192 and 16384, print one JSON "
                          "object with the measured dense bf16 MFMA rate and exit (context for "
                          "the spec peak the roofline uses)")
+    ap.add_argument("--varlen-calls", action="store_true",
+                    help="the 16 variable-length prompts (N in [36000, 40000], H = 14) as 16 "
+                         "separate forwards on the one build: per call the median and best of "
+                         "--steps timed forwards, effective TFLOP/s and densities, then the "
+                         "worst / median time per FLOP; one JSON object, then exit")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="per-kernel durations (all, timed window, cold window) from a rocprofv3 "
                          "kernel-trace CSV of a bench run with the same --warmup/--steps; no GPU")
@@ -402,6 +457,9 @@ def main() -> int:
 
     import block_sparse_attention_sol_amd as sol
     import synth
+
+    if args.varlen_calls:
+        return varlen_calls(args, sol, synth)
 
     packed = args.workload == "varlen_packed"
     dev = torch.device("cuda:0")
