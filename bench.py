@@ -308,17 +308,18 @@ def varlen_calls(args, sol, synth) -> int:
     import torch
     calls = synth.varlen_calls()
     rows, first_ms = [], None
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0, evm, ev1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     for n, w in enumerate(calls):
         q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda:0")
                    for x in synth.make_qkv(w))
         o = torch.empty_like(q)
         ws = torch.empty(max(sol.route_workspace_bytes(q), 256), dtype=torch.uint8, device=q.device)
         outs = sol.route_outputs(q)
-        ts = []
+        ts, tr, ta = [], [], []
         for rep in range(args.steps + 1):
             ev0.record()
             sol.route(q, k, w.tau, w.sink, workspace=ws, out=outs)
+            evm.record()
             sol.attn(q, k, v, outs[0], outs[1], w.sink, out=o, order=outs[3])
             ev1.record()
             torch.cuda.synchronize()
@@ -327,13 +328,18 @@ def varlen_calls(args, sol, synth) -> int:
                 first_ms = t
             if rep > 0:
                 ts.append(t)
+                tr.append(ev0.elapsed_time(evm))
+                ta.append(evm.elapsed_time(ev1))
         tot = outs[2].cpu().numpy()
         nb = sol.num_blocks(w.N)
         ncand = nb - (nb if w.sink >= w.N else w.sink // 64)
         flop = 4.0 * w.D * int(tot[1])
         med, best = float(np.median(ts)), float(min(ts))
         rows.append({"N": w.N, "median_ms": round(med, 4), "best_ms": round(best, 4),
+                     "route_ms": round(float(np.median(tr)), 4),
+                     "attn_ms": round(float(np.median(ta)), 4),
                      "tflops_median": round(flop / med / 1e9, 1),
+                     "attn_tflops": round(flop / float(np.median(ta)) / 1e9, 1),
                      "route_density": round(int(tot[0]) / (w.B * w.H * nb * ncand), 6),
                      "effective_flop": flop})
         err(f"{w.name}: N={w.N} median {med:.3f} ms, best {best:.3f} ms, "
