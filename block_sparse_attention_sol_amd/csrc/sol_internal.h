@@ -69,8 +69,9 @@ __device__ __forceinline__ int xcd_remap(int wg, int grid, int total) {
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-// Routing launch: pool + score/select (+ schedule when order != nullptr).
-// ws holds qbar, kbar, then the scoring workgroups' partial totals.
+// Routing launch: K pooling, then scoring with the query blocks pooled on chip
+// (+ schedule when order != nullptr).  ws holds room for qbar (unused here),
+// kbar, then the scoring workgroups' partial totals.
 hipError_t launch_route(const Geom& g, const void* q, const void* k, float scale, float tau,
                         int16_t* idx, int32_t* cnt, int64_t* totals, int32_t* order, float* ws,
                         hipStream_t stream);
