@@ -193,6 +193,17 @@ def test_maximum_candidates(sol, maxcand_inputs, tau):
     _run(sol, w, blocks=sample_blocks(g, 1, 1, 12, seed=5), tau=tau, inputs=inputs)
 
 
+def test_maximum_candidates_head_dim_64(sol):
+    """The 4096-candidate limit at D = 64 and two heads: routing bit for bit,
+    attention on sampled blocks of both heads (first, straddle, last
+    included)."""
+    w = synth.Workload("maxcand64", B=1, N=263000, H=2, D=64, sink=951, tau=0.5, kind="field",
+                       alpha=1.0, seed=12)
+    g = orc.geometry(w.N, w.sink)
+    assert g.ncand == 4096
+    _run(sol, w, blocks=sample_blocks(g, 1, 2, 12, seed=6))
+
+
 @pytest.mark.parametrize("N,D", [(1, 64), (200, 128), (1000, 64), (3001, 128)])
 def test_dense_parity_edge_shapes(sol, N, D):
     w = synth.Workload("dense_edge", B=1, N=N, H=2, D=D, sink=0, tau=math.inf, kind="field",
